@@ -1,0 +1,102 @@
+"""Shared test helpers: host conversions and tiny hand-built paged problems.
+
+Nothing here computes attention; the helpers only lay inputs out.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from paged_gqa_attention_pa_amd import workloads
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round fp32 values to bf16 (RNE, via torch) and return the uint16 bits."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bits_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def batch_to_oracle(batch: workloads.Batch) -> oracle.PagedInputs:
+    """Host copy of a generated batch, in the oracle's input form."""
+    qsl = None if batch.query_start_loc is None else batch.query_start_loc.cpu().numpy()
+    return oracle.PagedInputs(
+        q=workloads.bf16_bits(batch.q), k_pool=workloads.bf16_bits(batch.k_pool),
+        v_pool=workloads.bf16_bits(batch.v_pool),
+        block_tables=batch.block_tables.cpu().numpy(),
+        context_lens=batch.context_lens.cpu().numpy(), query_start_loc=qsl,
+        num_kv_heads=batch.spec.num_kv_heads, page_size=batch.spec.page_size,
+        strides=batch.kv_strides(), scale=batch.spec.scale, causal=batch.spec.causal)
+
+
+class DenseProblem:
+    """A paged problem whose pages sit in order (identity block table over a
+    contiguous cache), so the dense per-sequence K and V are plain slices.
+
+    k_dense[s], v_dense[s]: fp64 [L_s, Hkv, D];  q: fp64 [T, Hq, D].
+    """
+
+    def __init__(self, seed, contexts, queries, Hq, Hkv, D, P=16, causal=True,
+                 scale=None, decode_layout=None, q_gain=1.0):
+        rng = np.random.default_rng(seed)
+        self.contexts, self.queries = list(contexts), list(queries)
+        B = len(contexts)
+        pages = [-(-c // P) for c in contexts]
+        npages = max(sum(pages), 1)
+        max_blocks = max(max(pages) if pages else 1, 1)
+        bt = np.full((B, max_blocks), -1, dtype=np.int32)
+        base = 0
+        for s, n in enumerate(pages):
+            bt[s, :n] = np.arange(base, base + n, dtype=np.int32)
+            base += n
+        T = sum(queries)
+        qf = rng.standard_normal((T, Hq, D)).astype(np.float32) * np.float32(q_gain)
+        kf = rng.standard_normal((npages, P, Hkv, D)).astype(np.float32)
+        vf = rng.standard_normal((npages, P, Hkv, D)).astype(np.float32)
+        self.q_bits = f32_to_bf16_bits(qf)
+        self.k_bits = f32_to_bf16_bits(kf)
+        self.v_bits = f32_to_bf16_bits(vf)
+        if decode_layout is None:
+            decode_layout = all(q == 1 for q in queries)
+        qsl = None if decode_layout else np.concatenate([[0], np.cumsum(queries)]).astype(np.int32)
+        if scale is None:
+            scale = float(np.float32(1.0 / np.sqrt(D)))
+        self.scale = scale
+        self.P, self.Hq, self.Hkv, self.D = P, Hq, Hkv, D
+        self.bt = bt
+        self.qsl = qsl
+        self.causal = causal
+        self.inputs = self.make_inputs()
+        kd = bits_to_f64(self.k_bits).reshape(npages * P, Hkv, D)
+        vd = bits_to_f64(self.v_bits).reshape(npages * P, Hkv, D)
+        self.q = bits_to_f64(self.q_bits)
+        self.k_dense, self.v_dense = [], []
+        base = 0
+        for s, c in enumerate(contexts):
+            self.k_dense.append(kd[base * P: base * P + c])
+            self.v_dense.append(vd[base * P: base * P + c])
+            base += pages[s]
+
+    def make_inputs(self, k_bits=None, v_bits=None, bt=None, q_bits=None, contexts=None,
+                    qsl="same", causal=None, Hkv=None) -> oracle.PagedInputs:
+        k = self.k_bits if k_bits is None else k_bits
+        v = self.v_bits if v_bits is None else v_bits
+        hkv = self.Hkv if Hkv is None else Hkv
+        strides = (self.P * hkv * self.D, hkv * self.D, self.D)
+        return oracle.PagedInputs(
+            q=self.q_bits if q_bits is None else q_bits, k_pool=k, v_pool=v,
+            block_tables=self.bt if bt is None else bt,
+            context_lens=np.asarray(self.contexts if contexts is None else contexts,
+                                    dtype=np.int32),
+            query_start_loc=self.qsl if isinstance(qsl, str) else qsl,
+            num_kv_heads=hkv, page_size=self.P, strides=strides, scale=self.scale,
+            causal=self.causal if causal is None else causal)
+
+    def token_range(self, s):
+        start = sum(self.queries[:s])
+        return start, start + self.queries[s]
