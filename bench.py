@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark: paged GQA attention on one MI355X.
+
+Default workload: long-context decode (batch 1, 32 query / 8 KV heads,
+head_dim 128, context 32768, page size 16, shuffled pages in a 4096-page
+pool, bf16) with split-KV and the log-sum-exp merge.  One step = one decode
+call (every stage of the path) for the whole batch, replayed from a HIP
+graph.  Each step reads a different copy of the K/V pools (--pools copies,
+together far larger than the 256 MiB Infinity Cache), so every step streams
+its KV bytes from HBM.
+
+Reported: decode KV GB/s = 4096 bytes per context token (8 KV heads x K and
+V x 128 x 2 bytes) x context tokens / step time.  Alongside: the roofline of
+the decode launch (HIP events around every replay, on the replay stream), a
+secondary prefill line (causal chunked prefill 4 x (1024 + 2048), TFLOP/s
+over the causally allowed pairs, 4*D flops per (query, key, head)), and the
+fp64 oracle timed on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+DECODE_BYTES_PER_TOKEN = 4096
+
+
+def note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_ctx32k")
+    ap.add_argument("--pools", type=int, default=6, help="K/V pool copies cycled over steps")
+    ap.add_argument("--splits", type=int, default=0, help="force num_splits (0 = table)")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def decode_bytes(b):
+    return int(b.context_lens.sum().item()) * DECODE_BYTES_PER_TOKEN
+
+
+def prefill_flops(b):
+    """4*D flops per causally allowed (query, key, q-head) triple."""
+    D, Hq = b.spec.head_dim, b.spec.num_q_heads
+    total = 0
+    for L, q in zip(b.context_lens.tolist(), b.query_lens):
+        # query i (0-based) of the chunk sees L - q + i + 1 keys
+        total += q * (L - q) + q * (q + 1) // 2 if b.spec.causal else q * L
+    return 4 * D * Hq * total
+
+
+def time_replays(torch, graphs, steps, warmup):
+    """Replay graphs round-robin; events around every replay on the replay
+    stream.  Returns (total ms, per-replay ms list)."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]), per
+
+
+def bench_decode(torch, pa, workloads, args, dev):
+    spec = workloads.WORKLOADS[args.workload]
+    if not spec.decode_layout:
+        raise SystemExit(f"{args.workload} is not a decode workload")
+    b = workloads.generate(spec, dev, fill="zero")
+    note(f"generated {spec.name}: B={b.num_seqs} max_ctx={b.max_context_len}")
+    pools = [(b.k_pool, b.v_pool)]
+    for _ in range(max(1, args.pools) - 1):
+        pools.append((b.k_pool.clone(), b.v_pool.clone()))
+    max_ctx = b.max_context_len  # host bound, read once outside any capture
+    problem = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale, max_ctx, 1)
+    tiles, ws = pa.select_tiles(problem)
+    if args.splits:
+        tiles.num_splits = args.splits
+        ws = pa.workspace_size(problem, tiles)
+    workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)
+
+    def step(kp, vp):
+        pa.decode(b.q, kp, vp, b.block_tables, b.context_lens, spec.scale, max_ctx,
+                  out=out, tiles=tiles, workspace=workspace, problem=problem)
+
+    for kp, vp in pools:  # eager warm-up (and first-launch costs) outside capture
+        step(kp, vp)
+    torch.cuda.synchronize()
+    graphs = []
+    for kp, vp in pools:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(kp, vp)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    note(f"captured {len(graphs)} decode graphs, tiles={tiles.as_dict()}")
+    total_ms, per = time_replays(torch, graphs, args.steps, args.warmup)
+    nbytes = decode_bytes(b)
+    return dict(batch=b, tiles=tiles, total_ms=total_ms, per=per, nbytes=nbytes,
+                pool_bytes=sum(p[0].numel() * 2 * 2 for p in pools))
+
+
+def bench_prefill(torch, pa, workloads, dev, steps, warmup):
+    spec = workloads.WORKLOADS["prefill_chunk2048"]
+    b = workloads.generate(spec, dev, fill="zero")
+    max_ctx, max_q = b.max_context_len, b.max_query_len
+    problem = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                              max_ctx, max_q, causal=spec.causal)
+    tiles, ws = pa.select_tiles(problem)
+    workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        pa.prefill(b.q, b.query_start_loc, b.k_pool, b.v_pool, b.block_tables, b.context_lens,
+                   spec.scale, max_ctx, max_q, causal=spec.causal,
+                   out=out, tiles=tiles, workspace=workspace, problem=problem)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    total_ms, per = time_replays(torch, [g], steps, warmup)
+    flops = prefill_flops(b)
+    avg_ms = sum(per) / len(per)
+    tfs = flops / (avg_ms * 1e-3) / 1e12
+    return {"workload": "prefill_chunk2048 (B=4, 1024 cached + 2048 new tokens, causal)",
+            "metric": "prefill attention TFLOP/s (causal pairs, 4*D flop each)",
+            "value": round(tfs, 2), "unit": "TFLOP/s", "ms_per_step": round(avg_ms, 4),
+            "tiles": tiles.as_dict(),
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2),
+                         "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None}}
+
+
+def cpu_baseline(workloads, b, seconds):
+    """The fp64 oracle on the same decode workload, on the host cores."""
+    import oracle
+    import numpy as np
+    qsl = None
+    inp = oracle.PagedInputs(
+        q=workloads.bf16_bits(b.q), k_pool=workloads.bf16_bits(b.k_pool),
+        v_pool=workloads.bf16_bits(b.v_pool), block_tables=b.block_tables.cpu().numpy(),
+        context_lens=b.context_lens.cpu().numpy(), query_start_loc=qsl,
+        num_kv_heads=b.spec.num_kv_heads, page_size=b.spec.page_size,
+        strides=b.kv_strides(), scale=b.spec.scale, causal=b.spec.causal)
+    threads = oracle.default_threads()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(inp, threads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 1000:
+            break
+    gbs = decode_bytes(b) * runs / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole {b.spec.name} batch (all {b.q.shape[0] * b.q.shape[1]} query "
+                      f"rows), {runs} run(s) in {el:.1f} s, fp64, {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library is a "
+              "single-GPU kernel library; see DESIGN.md for how the path would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_gqa_attention_pa_amd import pa, workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa.load()
+    dev = torch.device("cuda:0")
+
+    d = bench_decode(torch, pa, workloads, args, dev)
+    b = d["batch"]
+    ms_per_step = d["total_ms"] / args.steps
+    value = d["nbytes"] / (ms_per_step * 1e-3) / 1e9
+    avg_launch_ms = sum(d["per"]) / len(d["per"])
+    achieved = d["nbytes"] / (avg_launch_ms * 1e-3) / 1e9
+    note(f"decode: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s")
+
+    result = {
+        "metric": "decode KV GB/s (% of HBM peak); prefill attention TFLOP/s (% MFMA peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, Llama-3.1-8B-shaped attention, no weights)",
+        "config": {
+            "workload": f"{b.spec.name}: decode, batch {b.num_seqs}, context "
+                        f"{b.max_context_len}, 32 q / 8 kv heads, head_dim 128, page 16, "
+                        f"pool {b.spec.pool_pages} pages",
+            "num_splits": d["tiles"].num_splits,
+            "pool_copies": args.pools,
+            "kv_bytes_per_step": d["nbytes"],
+            "graph": "hipGraph replay",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+        },
+    }
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(torch, pa, workloads, dev, max(5, args.steps // 5),
+                                          min(args.warmup, 3))
+        note(f"prefill: {result['prefill']['value']} TFLOP/s")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(workloads, b, args.cpu_seconds)
+        note(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

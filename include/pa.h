@@ -1,0 +1,164 @@
+/*
+ * pa.h - C ABI of the MI355X (gfx950) paged grouped-query attention library.
+ *
+ * Pages cited (by short name):
+ *   [IBM-PA]  "一行 Triton 代码同时跑赢 NVIDIA 和 AMD：IBM Research 把大模型推理的
+ *             「硬件鸿沟」填平了" (papers.ananclaw.com, summary of arXiv 2511.11581)
+ *   [GUIDE]   "从兆字节到兆瓦：基于CUDA与Triton的高性能LLM与扩散内核全指南"
+ *             (zhxwu.com GPU programming guide)
+ *
+ * The operation: for every query token t of sequence s and query head h,
+ *   out[t, h, :] = softmax_j( scale * q[t, h, :] . K_s[j, h / G, :] ) V_s[j, h / G, :]
+ * over the allowed keys j of that sequence (the SDPA definition, [GUIDE]
+ * section "拆解多头注意力（MHA）"), where G = num_q_heads / num_kv_heads groups
+ * query heads onto a shared KV head ([IBM-PA] five-step list, Q-Block step),
+ * and K_s, V_s are read through the sequence's block table from paged pools
+ * ([IBM-PA] model-feature list: paged KV cache, prefix cache).
+ * Allowed keys: j < context_lens[s]; with causal set, also
+ * j <= context_lens[s] - q_len(s) + i for the i-th new query token of s
+ * (future scores are minus infinity, [GUIDE] section "Triton实现Flash
+ * Attention", causal item; the new tokens are the last q_len(s) positions of
+ * the context, so a chunk attends to the cached prefix and causally to itself).
+ * No allowed key: out = 0, lse = -inf.
+ *
+ * Layouts (element = one bf16 unless stated):
+ *   q, out        packed [T, Hq, D], row-major, T query tokens
+ *   k_pool/v_pool element (page, slot, kv_head, d) sits at
+ *                 page*kv_stride_page + slot*kv_stride_token
+ *                 + kv_head*kv_stride_head + d   (d stride is 1)
+ *                 K and V share the strides.  Default: [pages, P, Hkv, D].
+ *   block_tables  int32 [B, max_blocks_per_seq]; entry b of row s is the
+ *                 page holding logical tokens [b*P, (b+1)*P) of sequence s.
+ *                 Entries past ceil(context_lens[s]/P) are never read.
+ *   context_lens  int32 [B]; the cached tokens of s, new tokens included.
+ *   query_start_loc int32 [B+1] (prefill): tokens of s are rows
+ *                 [query_start_loc[s], query_start_loc[s+1]) of q and out.
+ *   lse           fp32 [T, Hq], natural log of the softmax denominator
+ *                 sum_j exp(scale * q.k_j); optional (NULL to skip).
+ *
+ * Ownership and threading: every pointer is device memory owned by the
+ * caller.  The compute calls never allocate, free or synchronise; they only
+ * enqueue kernels on the caller's stream, so they can be captured in a HIP
+ * graph.  Lengths, tables and query_start_loc are read on the device only;
+ * the grid depends only on host fields of pa_problem (a static launch grid,
+ * [IBM-PA] five-step list, static-grid and graph steps).  The library has
+ * no mutable global state.
+ *
+ * Errors: every host-side argument is checked before anything is enqueued;
+ * a failed check returns a status and enqueues nothing.  A failed launch
+ * returns PA_ERR_HIP.  Device-side data is trusted: a block-table entry
+ * outside the pool, a context longer than max_context_len or than
+ * max_blocks_per_seq*P, or a query length above max_query_len is undefined
+ * behaviour.  Nothing aborts and no exception crosses the ABI.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment          */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, page size, G    */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
+  PA_ERR_HIP = 4          /* a HIP launch failed                            */
+} pa_status;
+
+typedef enum pa_dtype { PA_BF16 = 0, PA_FP32 = 1 } pa_dtype;
+
+/* Host description of one call.  Every field is read on the host only. */
+typedef struct pa_problem {
+  int32_t num_seqs;           /* B >= 0                                         */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads                 */
+  int32_t num_kv_heads;       /* Hkv                                            */
+  int32_t head_dim;           /* D; 128 is built                                */
+  int32_t page_size;          /* P; 16 is built                                 */
+  int32_t max_blocks_per_seq; /* row stride of block_tables                     */
+  int64_t kv_stride_page;     /* pool strides in elements, multiples of 8       */
+  int64_t kv_stride_token;
+  int64_t kv_stride_head;
+  int32_t max_context_len;    /* bound on every context_lens[s] (sizes the grid) */
+  int32_t max_query_len;      /* bound on every query length; 1 for decode      */
+  int32_t total_query_tokens; /* T: rows of q and out                           */
+  int32_t causal;             /* 0 or 1 (decode rows are unaffected)            */
+  float scale;                /* multiplies q.k; e.g. 1/sqrt(D)                 */
+  pa_dtype out_dtype;         /* PA_BF16 or PA_FP32                             */
+} pa_problem;
+
+/* Launch shape chosen by pa_select_tiles (or forced by a tuning sweep). */
+typedef struct pa_tiles {
+  int32_t kv_tile;           /* keys per inner step (16 decode; 32/64 prefill)   */
+  int32_t num_splits;        /* split-KV count S (>= 1)                          */
+  int32_t waves_per_wg;      /* wavefronts per workgroup                         */
+  int32_t q_tokens_per_tile; /* query tokens per prefill workgroup               */
+  int32_t variant;           /* bit 0 (prefill): carry P as a bf16 high part plus a  */
+                             /* bf16 remainder in P.V (relative weight error ~2^-18  */
+                             /* instead of ~2^-9); chosen for fp32 outputs           */
+} pa_tiles;
+
+/* Pick the launch shape for a problem from the built-in table (the offline
+ * decision table of [IBM-PA] section on moving autotuning offline), and the
+ * workspace size the compute call needs.  Pure host code: no HIP call.
+ * out and workspace_bytes may not be NULL. */
+pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* workspace_bytes);
+
+/* Workspace bytes a given launch shape needs (0 when num_splits == 1). */
+pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
+                            size_t* workspace_bytes);
+
+/* Decode: one query token per sequence (T = num_seqs, row s of q belongs to
+ * sequence s; causal has no effect).  Split-KV ([IBM-PA] five-step list,
+ * parallel tiled softmax step): with tiles->num_splits = S > 1 the context of
+ * each sequence is cut into S contiguous, page-aligned ranges processed by
+ * different workgroups; their (normalised output, lse) partials go to the
+ * workspace and are merged by log-sum-exp in the same call.
+ * q: bf16 [B, Hq, D]; out: [B, Hq, D] of problem->out_dtype; lse: fp32
+ * [B, Hq] or NULL.  workspace: >= pa_workspace_size bytes, 256-byte aligned,
+ * may be NULL when that size is 0.  Pointers to bf16 data must be 16-byte
+ * aligned. */
+pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                    const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                    const int32_t* context_lens, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* Prefill / chunked prefill / mixed batch in one launch: sequence s owns
+ * query rows [query_start_loc[s], query_start_loc[s+1]); those tokens are
+ * the last q_len(s) positions of its context (already written to the pages),
+ * so they attend to the cached prefix and, with causal set, causally to each
+ * other.  Query length 1 rows (decode sequences) may be mixed in.
+ * q: bf16 [T, Hq, D]; out: [T, Hq, D] of out_dtype; lse: fp32 [T, Hq] or NULL.
+ * Workspace as for pa_decode. */
+pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                     const int32_t* query_start_loc, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Log-sum-exp merge of split partials (the merge that makes the parallel
+ * tiled softmax of [IBM-PA] exact; its algebra is that of the online-softmax
+ * statistics m and l, [GUIDE] section "Flash Attention革命").  Per row r:
+ *   M = max_k lse_k; w_k = exp(lse_k - M);
+ *   out[r] = sum_k w_k O_k / sum_k w_k;  lse_out[r] = M + ln sum_k w_k;
+ *   every lse_k = -inf gives out[r] = 0 and lse_out[r] = -inf.
+ * partial_o: fp32 [rows, S, head_dim] (normalised per split); partial_lse:
+ * fp32 [rows, S]; out: [rows, head_dim] of out_dtype; lse_out: fp32 [rows]
+ * or NULL.  head_dim must be a positive multiple of 4 (at most 1024). */
+pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, int32_t rows,
+                            int32_t num_splits, int32_t head_dim, void* out,
+                            pa_dtype out_dtype, float* lse_out, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,242 @@
+// C ABI of the paged GQA attention library: argument checks, launch-shape
+// selection, workspace sizing, and the launches.  Host code only; every
+// check runs before anything is enqueued.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+#include "pa_tile_table.h"
+
+namespace {
+
+using pa::kHeadDim;
+using pa::kPage;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+bool group_built(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Checks shared by every call; returns PA_OK or the first failure.
+pa_status check_problem(const pa_problem* pb) {
+  if (!pb) return PA_ERR_INVALID_ARG;
+  if (pb->num_seqs < 0 || pb->num_q_heads <= 0 || pb->num_kv_heads <= 0 || pb->head_dim <= 0 ||
+      pb->page_size <= 0 || pb->max_blocks_per_seq <= 0 || pb->max_context_len < 0 ||
+      pb->max_query_len < 0 || pb->total_query_tokens < 0)
+    return PA_ERR_INVALID_ARG;
+  if (pb->num_q_heads % pb->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if ((pb->page_size & (pb->page_size - 1)) != 0) return PA_ERR_INVALID_ARG;
+  if (pb->kv_stride_page <= 0 || pb->kv_stride_token <= 0 || pb->kv_stride_head <= 0 ||
+      pb->kv_stride_page % 8 || pb->kv_stride_token % 8 || pb->kv_stride_head % 8)
+    return PA_ERR_INVALID_ARG;
+  if (pb->out_dtype != PA_BF16 && pb->out_dtype != PA_FP32) return PA_ERR_INVALID_ARG;
+  if (pb->causal != 0 && pb->causal != 1) return PA_ERR_INVALID_ARG;
+  if (!(pb->scale == pb->scale)) return PA_ERR_INVALID_ARG;  // NaN scale
+  if ((int64_t)pb->max_context_len > (int64_t)pb->max_blocks_per_seq * pb->page_size)
+    return PA_ERR_INVALID_ARG;
+  if (pb->head_dim != kHeadDim || pb->page_size != kPage) return PA_ERR_UNSUPPORTED;
+  if (!group_built(pb->num_q_heads / pb->num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+pa_status check_tiles(const pa_tiles* t) {
+  if (!t) return PA_ERR_INVALID_ARG;
+  if (t->num_splits < 1 || t->num_splits > pa::kMaxSplits) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+size_t partial_bytes(int64_t rows, int splits, int head_dim) {
+  if (splits <= 1) return 0;
+  return align_up((size_t)rows * splits * head_dim * sizeof(float)) +
+         align_up((size_t)rows * splits * sizeof(float));
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape (not built)";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
+                            size_t* workspace_bytes) {
+  pa_status st = check_problem(problem);
+  if (st != PA_OK) return st;
+  if ((st = check_tiles(tiles)) != PA_OK) return st;
+  if (!workspace_bytes) return PA_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)problem->max_query_len <= 1
+                           ? (int64_t)problem->num_seqs * problem->num_q_heads
+                           : (int64_t)problem->total_query_tokens * problem->num_q_heads;
+  *workspace_bytes = partial_bytes(rows, tiles->num_splits, problem->head_dim);
+  return PA_OK;
+}
+
+pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* workspace_bytes) {
+  pa_status st = check_problem(problem);
+  if (st != PA_OK) return st;
+  if (!out || !workspace_bytes) return PA_ERR_INVALID_ARG;
+  const int G = problem->num_q_heads / problem->num_kv_heads;
+  pa_tiles t;
+  memset(&t, 0, sizeof t);
+  if (problem->max_query_len <= 1) {
+    t.kv_tile = pa::kDecodeTile;
+    t.waves_per_wg = 4;
+    t.q_tokens_per_tile = 1;
+    t.num_splits = pa::table_decode_splits(problem->num_seqs, problem->num_kv_heads,
+                                           problem->max_context_len);
+  } else {
+    t.kv_tile = 32;
+    t.waves_per_wg = 4;
+    t.q_tokens_per_tile = 128 / G;
+    t.num_splits = 1;
+    // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18
+    t.variant = problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0;
+  }
+  *out = t;
+  return pa_workspace_size(problem, &t, workspace_bytes);
+}
+
+pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                    const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                    const int32_t* context_lens, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  pa_status st = check_problem(problem);
+  if (st != PA_OK) return st;
+  if ((st = check_tiles(tiles)) != PA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  const int S = tiles->num_splits;
+  const int64_t rows = (int64_t)problem->num_seqs * problem->num_q_heads;
+  const size_t need = partial_bytes(rows, S, problem->head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+    return PA_ERR_WORKSPACE;
+  if (problem->num_seqs == 0) return PA_OK;
+
+  const int G = problem->num_q_heads / problem->num_kv_heads;
+  const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
+  pa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = static_cast<const uint16_t*>(k_pool);
+  p.v_pool = static_cast<const uint16_t*>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  if (S > 1) {
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align_up((size_t)rows * S * problem->head_dim * sizeof(float)));
+  }
+  p.stride_page = problem->kv_stride_page;
+  p.stride_token = problem->kv_stride_token;
+  p.stride_head = problem->kv_stride_head;
+  p.num_seqs = problem->num_seqs;
+  p.num_q_heads = problem->num_q_heads;
+  p.num_kv_heads = problem->num_kv_heads;
+  p.max_blocks = problem->max_blocks_per_seq;
+  p.num_splits = S;
+  p.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
+  p.scale_log2 = problem->scale * pa::kLog2eHost;
+  p.out_f32 = problem->out_dtype == PA_FP32;
+  if ((st = from_hip(pa::launch_decode(p, G, stream))) != PA_OK) return st;
+  if (S > 1) {
+    pa::ReduceParams r;
+    r.part_o = p.part_o;
+    r.part_lse = p.part_lse;
+    r.out = out;
+    r.lse = lse;
+    r.rows = (int32_t)rows;
+    r.num_splits = S;
+    r.head_dim = problem->head_dim;
+    r.out_f32 = p.out_f32;
+    if ((st = from_hip(pa::launch_reduce(r, stream))) != PA_OK) return st;
+  }
+  return PA_OK;
+}
+
+pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                     const int32_t* query_start_loc, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  pa_status st = check_problem(problem);
+  if (st != PA_OK) return st;
+  if ((st = check_tiles(tiles)) != PA_OK) return st;
+  if (tiles->num_splits != 1) return PA_ERR_UNSUPPORTED;
+  if (!q || !query_start_loc || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  if (problem->num_seqs == 0 || problem->total_query_tokens == 0) return PA_OK;
+  const int G = problem->num_q_heads / problem->num_kv_heads;
+  const int qt = 128 / G;
+  pa::PrefillParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.query_start_loc = query_start_loc;
+  p.k_pool = static_cast<const uint16_t*>(k_pool);
+  p.v_pool = static_cast<const uint16_t*>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.lse = lse;
+  p.stride_page = problem->kv_stride_page;
+  p.stride_token = problem->kv_stride_token;
+  p.stride_head = problem->kv_stride_head;
+  p.num_seqs = problem->num_seqs;
+  p.num_q_heads = problem->num_q_heads;
+  p.num_kv_heads = problem->num_kv_heads;
+  p.max_blocks = problem->max_blocks_per_seq;
+  p.q_tile = qt;
+  p.causal = problem->causal;
+  p.scale_log2 = problem->scale * pa::kLog2eHost;
+  p.out_f32 = problem->out_dtype == PA_FP32;
+  // static grid: sum over sequences of ceil(q_len / qt) <= ceil(T / qt) + B
+  const int64_t grid_x = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
+  if (grid_x > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  return from_hip(pa::launch_prefill(p, G, (int)grid_x,
+                                    (tiles->variant & pa::kVariantPreciseP) != 0, stream));
+}
+
+pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, int32_t rows,
+                            int32_t num_splits, int32_t head_dim, void* out,
+                            pa_dtype out_dtype, float* lse_out, hipStream_t stream) {
+  if (rows < 0 || num_splits < 1 || head_dim <= 0 || head_dim % 4 != 0 || head_dim > 1024)
+    return PA_ERR_INVALID_ARG;
+  if (out_dtype != PA_BF16 && out_dtype != PA_FP32) return PA_ERR_INVALID_ARG;
+  if (rows == 0) return PA_OK;
+  if (!partial_o || !partial_lse || !out) return PA_ERR_INVALID_ARG;
+  if (!aligned16(partial_o) || !aligned16(out)) return PA_ERR_INVALID_ARG;
+  pa::ReduceParams r;
+  r.part_o = partial_o;
+  r.part_lse = partial_lse;
+  r.out = out;
+  r.lse = lse_out;
+  r.rows = rows;
+  r.num_splits = num_splits;
+  r.head_dim = head_dim;
+  r.out_f32 = out_dtype == PA_FP32;
+  return from_hip(pa::launch_reduce(r, stream));
+}
+
+}  // extern "C"

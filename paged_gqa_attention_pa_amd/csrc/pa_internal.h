@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI host code and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kHeadDim = 128;   // built head dimension
+constexpr int kPage = 16;       // built page size
+constexpr int kDecodeTile = 16; // keys per decode step (one MFMA N-tile)
+constexpr int kMaxSplits = 256;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// pa_tiles.variant bits
+constexpr int kVariantPreciseP = 1;  // prefill: P as bf16 high + remainder
+
+struct DecodeParams {
+  const uint16_t* q;        // [B, Hq, D] bf16
+  const uint16_t* k_pool;   // paged pools, bf16
+  const uint16_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;                // [B, Hq, D] bf16 or fp32
+  float* lse;               // [B, Hq] or null
+  float* part_o;            // [B*Hq, S, D] when S > 1
+  float* part_lse;          // [B*Hq, S]
+  int64_t stride_page, stride_token, stride_head;
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
+  int32_t tiles_per_split;  // 16-key tiles per split
+  int32_t num_splits;
+  float scale_log2;         // scale * log2(e)
+  int32_t out_f32;
+};
+
+struct PrefillParams {
+  const uint16_t* q;        // [T, Hq, D] bf16
+  const int32_t* query_start_loc;  // [B+1]
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;                // [T, Hq, D]
+  float* lse;               // [T, Hq] or null
+  int64_t stride_page, stride_token, stride_head;
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
+  int32_t q_tile;           // query tokens per workgroup
+  int32_t causal;
+  float scale_log2;
+  int32_t out_f32;
+};
+
+struct ReduceParams {
+  const float* part_o;      // [rows, S, D]
+  const float* part_lse;    // [rows, S]
+  void* out;                // [rows, D]
+  float* lse;               // [rows] or null
+  int32_t rows, num_splits, head_dim, out_f32;
+};
+
+// Launchers: return hipSuccess or the launch error.  Shapes were checked.
+hipError_t launch_decode(const DecodeParams& p, int group, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int group, int grid_x, bool precise_p,
+                          hipStream_t stream);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+
+}  // namespace pa

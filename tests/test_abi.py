@@ -1,0 +1,126 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/pa.h
+declares, and its host-side checks reject bad arguments before any launch
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_gqa_attention_pa_amd import pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.library_path()):
+        pytest.skip("libpa.so not built (run __graft_entry__.build())")
+    return pa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(declared) == set(pa.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _problem(**kw):
+    pb = pa.Problem()
+    vals = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                max_blocks_per_seq=512, kv_stride_page=16 * 8 * 128, kv_stride_token=8 * 128,
+                kv_stride_head=128, max_context_len=8192, max_query_len=1,
+                total_query_tokens=4, causal=1, scale=0.08838834764831845,
+                out_dtype=pa.PA_BF16)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(pb, k, v)
+    return pb
+
+
+def _select(lib, pb):
+    t = pa.Tiles()
+    ws = ctypes.c_size_t(0)
+    st = lib.pa_select_tiles(ctypes.byref(pb), ctypes.byref(t), ctypes.byref(ws))
+    return st, t, ws.value
+
+
+def test_select_tiles_decode_and_prefill(lib):
+    st, t, ws = _select(lib, _problem())
+    assert st == pa.PA_OK and t.num_splits >= 1 and t.kv_tile == 16
+    if t.num_splits > 1:
+        assert ws >= 4 * 32 * t.num_splits * 129 * 4
+    # long context, batch 1: split-KV engages
+    st, t, ws = _select(lib, _problem(num_seqs=1, total_query_tokens=1, max_context_len=32768,
+                                      max_blocks_per_seq=2048))
+    assert st == pa.PA_OK and t.num_splits > 8 and ws > 0
+    st, t, ws = _select(lib, _problem(max_query_len=2048, total_query_tokens=8192,
+                                      max_context_len=3072))
+    assert st == pa.PA_OK and t.q_tokens_per_tile == 32 and t.num_splits == 1 and ws == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_q_heads", 30, pa.PA_ERR_INVALID_ARG),       # Hq % Hkv != 0
+    ("head_dim", 64, pa.PA_ERR_UNSUPPORTED),
+    ("page_size", 12, pa.PA_ERR_INVALID_ARG),         # not a power of two
+    ("page_size", 32, pa.PA_ERR_UNSUPPORTED),
+    ("kv_stride_token", 1020, pa.PA_ERR_INVALID_ARG),  # not a multiple of 8
+    ("max_context_len", 512 * 16 + 1, pa.PA_ERR_INVALID_ARG),
+    ("num_seqs", -1, pa.PA_ERR_INVALID_ARG),
+    ("out_dtype", 7, pa.PA_ERR_INVALID_ARG),
+    ("causal", 2, pa.PA_ERR_INVALID_ARG),
+    ("scale", float("nan"), pa.PA_ERR_INVALID_ARG),
+    ("num_kv_heads", 1, pa.PA_ERR_UNSUPPORTED),       # G = 32 not built
+])
+def test_select_tiles_rejects(lib, field, value, status):
+    st, _, _ = _select(lib, _problem(**{field: value}))
+    assert st == status
+
+
+def test_compute_calls_reject_before_launch(lib):
+    pb = _problem()
+    t = pa.Tiles(16, 1, 4, 1, 0)
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: checks fail first
+    nul = None
+    # null q
+    assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t), nul, fake, fake, fake, fake, fake,
+                         nul, nul, 0, nul) == pa.PA_ERR_INVALID_ARG
+    # misaligned q
+    mis = ctypes.c_void_p(0x10008)
+    assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t), mis, fake, fake, fake, fake, fake,
+                         nul, nul, 0, nul) == pa.PA_ERR_INVALID_ARG
+    # split-KV without workspace
+    t2 = pa.Tiles(16, 8, 4, 1, 0)
+    assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t2), fake, fake, fake, fake, fake, fake,
+                         nul, nul, 0, nul) == pa.PA_ERR_WORKSPACE
+    # too many splits
+    t3 = pa.Tiles(16, 100000, 4, 1, 0)
+    assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t3), fake, fake, fake, fake, fake, fake,
+                         nul, nul, 0, nul) == pa.PA_ERR_INVALID_ARG
+    # prefill without query_start_loc
+    pp = _problem(max_query_len=64, total_query_tokens=256)
+    assert lib.pa_prefill(ctypes.byref(pp), ctypes.byref(t), fake, nul, fake, fake, fake, fake,
+                          fake, nul, nul, 0, nul) == pa.PA_ERR_INVALID_ARG
+    # reduce: bad head_dim, bad dtype
+    assert lib.pa_splitkv_reduce(fake, fake, 4, 2, 126, fake, pa.PA_FP32, nul, nul) == \
+        pa.PA_ERR_INVALID_ARG
+    assert lib.pa_splitkv_reduce(fake, fake, 4, 2, 128, fake, 9, nul, nul) == \
+        pa.PA_ERR_INVALID_ARG
+    # empty batches are a no-op that launches nothing
+    assert lib.pa_decode(ctypes.byref(_problem(num_seqs=0, total_query_tokens=0)),
+                         ctypes.byref(t), fake, fake, fake, fake, fake, fake, nul, nul, 0,
+                         nul) == pa.PA_OK
+    assert lib.pa_splitkv_reduce(fake, fake, 0, 2, 128, fake, pa.PA_FP32, nul, nul) == pa.PA_OK
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert pa.status_string(s)
+    assert "workspace" in pa.status_string(pa.PA_ERR_WORKSPACE)

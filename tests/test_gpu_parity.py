@@ -1,0 +1,322 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (per element): fp32 outputs 2e-3; bf16 outputs 1e-2, widened to
+one bf16 ulp of the reference (2^-7 |ref|) where that is larger (|ref| >
+1.28), since rounding an exact result to bf16 alone can err by half an ulp;
+the natural-log LSE 2e-3.  Indexing cases (dominant
+logit, page permutation, NaN-poisoned stale slots) must match bit for bit.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _util import batch_to_oracle
+from paged_gqa_attention_pa_amd import pa, workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 1e-2, torch.float32: 2e-3}
+LSE_TOL = 2e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    return torch.device("cuda:0")
+
+
+def run_decode(b, out_dtype=torch.bfloat16, splits=None, with_lse=True):
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=b.q.device) if with_lse else None
+    tiles = None
+    if splits is not None:
+        pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, b.spec.scale,
+                             b.max_context_len, 1, out_dtype=out_dtype)
+        tiles, _ = pa.select_tiles(pb)
+        tiles.num_splits = splits
+    out = pa.decode(b.q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, b.spec.scale,
+                    b.max_context_len, out_dtype=out_dtype, lse=lse, tiles=tiles)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def run_prefill(b, out_dtype=torch.bfloat16, with_lse=True):
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=b.q.device) if with_lse else None
+    qsl = b.query_start_loc
+    if qsl is None:
+        qsl = torch.arange(b.num_seqs + 1, dtype=torch.int32, device=b.q.device)
+    out = pa.prefill(b.q, qsl, b.k_pool, b.v_pool, b.block_tables, b.context_lens,
+                     b.spec.scale, b.max_context_len, max(b.max_query_len, 1),
+                     causal=b.spec.causal, out_dtype=out_dtype, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def compare(b, out, lse, rows=None, label=""):
+    inp = batch_to_oracle(b)
+    ref, ref_lse = oracle.attention(inp, rows=rows)
+    D = b.spec.head_dim
+    got = out.float().cpu().numpy().reshape(-1, D)
+    got_lse = None if lse is None else lse.cpu().numpy().reshape(-1)
+    if rows is not None:
+        got = got[rows]
+        got_lse = None if got_lse is None else got_lse[rows]
+    tol = TOL[out.dtype]
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    diff = np.abs(got - ref)
+    err = float(np.max(diff)) if got.size else 0.0
+    log(f"{label}: rows={ref.shape[0]} max|err|={err:.3e} (tol {tol})")
+    if out.dtype == torch.bfloat16:
+        allowed = np.maximum(tol, 2.0 ** -7 * np.abs(ref))
+        worst = float(np.max(diff - allowed)) if got.size else -1.0
+        assert worst <= 0, f"{label}: error exceeds max(1e-2, 1 bf16 ulp) by {worst}"
+    else:
+        assert err <= tol, f"{label}: max|err| {err} > {tol}"
+    if got_lse is not None:
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(got_lse)), f"{label}: LSE finiteness differs"
+        if fin.any():
+            lerr = float(np.max(np.abs(got_lse[fin] - ref_lse[fin])))
+            assert lerr <= LSE_TOL, f"{label}: LSE err {lerr}"
+        assert np.all(got_lse[~fin] == -np.inf)
+    return err
+
+
+# ---------------------------------------------------------------- decode ----
+
+DECODE_CASES = [
+    ("ragged", [1, 15, 16, 17, 300, 1000, 0, 2049], 32, 8),
+    ("g1", [100, 33, 257], 8, 8),
+    ("g2", [100, 33, 257], 16, 8),
+    ("g8", [100, 33, 257], 32, 4),
+    ("g16", [100, 33, 257], 16, 1),
+]
+
+
+@pytest.mark.parametrize("name,ctx,hq,hkv", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+@pytest.mark.parametrize("splits", [None, 1, 3, 64])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_decode_small(dev, name, ctx, hq, hkv, splits, out_dtype):
+    log(f"[decode {name} splits={splits} {out_dtype}]")
+    spec = workloads.small_spec(f"dec_{name}", seed=100 + len(ctx) + hq, contexts=ctx,
+                                queries=[1] * len(ctx), num_q_heads=hq, num_kv_heads=hkv)
+    b = workloads.generate(spec, dev)
+    out, lse = run_decode(b, out_dtype, splits)
+    compare(b, out, lse, label=f"decode {name} S={splits}")
+
+
+def test_decode_logit_stress(dev):
+    log("[decode logit x8 stress]")
+    spec = workloads.small_spec("dec_stress", seed=7, contexts=[5000, 123], queries=[1, 1],
+                                logit_gain=8.0)
+    b = workloads.generate(spec, dev)
+    for dt in (torch.bfloat16, torch.float32):
+        out, lse = run_decode(b, dt)
+        compare(b, out, lse, label=f"decode stress {dt}")
+
+
+def _dominant_batch(dev, tstars, L, prefill_q=None):
+    qlen = [1] if prefill_q is None else [prefill_q]
+    spec = workloads.small_spec("dom", seed=31, contexts=[L] * len(tstars),
+                                queries=qlen * len(tstars))
+    b = workloads.generate(spec, dev)
+    P = spec.page_size
+    # q = 64 e_0 on every head; k_t*[0] = 64 on every KV head, k_t[0] = 0 elsewhere:
+    # z_t* = 4096 * scale ~ 362 and z_t = 0, so every other weight is exp(-362) -> 0.
+    b.q.zero_()
+    b.q[:, :, 0] = 64.0
+    for s, t in enumerate(tstars):
+        n = -(-L // P)
+        for j in range(n):
+            page = int(b.block_tables[s, j])
+            b.k_pool[page, :, :, 0] = 0.0
+        page = int(b.block_tables[s, t // P])
+        b.k_pool[page, t % P, :, 0] = 64.0
+    return b
+
+
+@pytest.mark.parametrize("splits", [1, 5, 64])
+def test_decode_dominant_logit_bitexact(dev, splits):
+    log(f"[decode dominant logit S={splits}]")
+    L = 1000
+    tstars = [0, 15, 16, 500, 511, 999]
+    b = _dominant_batch(dev, tstars, L)
+    for dt in (torch.bfloat16, torch.float32):
+        out, _ = run_decode(b, dt, splits)
+        for s, t in enumerate(tstars):
+            page = int(b.block_tables[s, t // 16])
+            v = b.v_pool[page, t % 16]  # [Hkv, D]
+            want = v.repeat_interleave(4, dim=0).to(dt)
+            assert torch.equal(out[s].view(torch.int16) if dt == torch.bfloat16 else out[s],
+                               want.view(torch.int16) if dt == torch.bfloat16 else want), \
+                f"seq {s} t*={t} {dt}"
+
+
+def _permuted(b):
+    """Same problem with every page moved elsewhere and the tables remapped."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(77)
+    npool = b.k_pool.shape[0]
+    perm = torch.randperm(npool, generator=g).to(b.k_pool.device)
+    k2 = torch.empty_like(b.k_pool)
+    v2 = torch.empty_like(b.v_pool)
+    k2[perm] = b.k_pool
+    v2[perm] = b.v_pool
+    bt2 = torch.where(b.block_tables >= 0, perm[b.block_tables.clamp(min=0).long()].int(),
+                      b.block_tables)
+    return workloads.Batch(spec=b.spec, q=b.q, k_pool=k2, v_pool=v2, block_tables=bt2,
+                           context_lens=b.context_lens, query_start_loc=b.query_start_loc,
+                           query_lens=b.query_lens, used_pages=b.used_pages)
+
+
+def test_decode_page_permutation_and_nan_bitexact(dev):
+    log("[decode permutation / NaN poison]")
+    spec = workloads.small_spec("perm", seed=41, contexts=[37, 1000, 16, 513], queries=[1] * 4,
+                                pool_slack=40)
+    b = workloads.generate(spec, dev, fill="nan")
+    bz = workloads.generate(spec, dev, fill="zero")
+    for splits in (1, 7):
+        o1, l1 = run_decode(b, torch.float32, splits)
+        o2, l2 = run_decode(_permuted(b), torch.float32, splits)
+        o3, l3 = run_decode(bz, torch.float32, splits)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert torch.equal(o1, o3) and torch.equal(l1, l3)
+        assert torch.isfinite(o1).all()
+
+
+# ---------------------------------------------------------------- prefill ---
+
+PREFILL_CASES = [
+    # (name, contexts, query lens, causal)
+    ("chunks", [300, 77, 1000, 33], [140, 77, 31, 33], True),
+    ("tiles", [32, 64, 65, 200], [32, 64, 65, 129], True),
+    ("noncausal", [300, 50], [100, 7], False),
+    ("decode_rows_first", [900, 40, 260, 513], [1, 1, 100, 200], True),
+    ("decode_rows_last", [260, 513, 900, 40], [100, 200, 1, 1], True),
+    ("degenerate", [0, 1, 5, 16], [0, 1, 5, 1], True),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql,causal", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_prefill_small(dev, name, ctx, ql, causal, out_dtype):
+    log(f"[prefill {name} {out_dtype}]")
+    spec = workloads.small_spec(f"pre_{name}", seed=200 + sum(ql), contexts=ctx, queries=ql,
+                                causal=causal, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    out, lse = run_prefill(b, out_dtype)
+    compare(b, out, lse, label=f"prefill {name}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 4), (16, 1)])
+def test_prefill_group_sizes(dev, hq, hkv):
+    log(f"[prefill G={hq // hkv}]")
+    spec = workloads.small_spec("pre_g", seed=300 + hq + hkv, contexts=[200, 90], queries=[70, 90],
+                                num_q_heads=hq, num_kv_heads=hkv, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    out, lse = run_prefill(b, torch.float32)
+    compare(b, out, lse, label=f"prefill G={hq // hkv}")
+
+
+def test_prefill_dominant_logit_bitexact(dev):
+    log("[prefill dominant logit]")
+    L, q = 300, 40
+    tstars = [0, 31, 32, 200, 259]  # all <= L - q, so every row of the chunk sees t*
+    b = _dominant_batch(dev, tstars, L, prefill_q=q)
+    for dt in (torch.bfloat16, torch.float32):
+        out, _ = run_prefill(b, dt)
+        for s, t in enumerate(tstars):
+            page = int(b.block_tables[s, t // 16])
+            want = b.v_pool[page, t % 16].repeat_interleave(4, dim=0).to(dt)
+            got = out[s * q:(s + 1) * q]
+            ok = (torch.equal(got.view(torch.int16), want.view(torch.int16).expand_as(got))
+                  if dt == torch.bfloat16 else torch.equal(got, want.expand_as(got)))
+            assert ok, f"seq {s} t*={t} {dt}"
+
+
+def test_prefill_page_permutation_and_nan_bitexact(dev):
+    log("[prefill permutation / NaN poison]")
+    spec = workloads.small_spec("pperm", seed=43, contexts=[301, 77, 40], queries=[150, 77, 1],
+                                pool_slack=30, decode_layout=False)
+    b = workloads.generate(spec, dev, fill="nan")
+    bz = workloads.generate(spec, dev, fill="zero")
+    o1, l1 = run_prefill(b, torch.float32)
+    o2, l2 = run_prefill(_permuted(b), torch.float32)
+    o3, l3 = run_prefill(bz, torch.float32)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+# ---------------------------------------------------------------- reduce ----
+
+@pytest.mark.parametrize("S", [1, 2, 7, 64, 256])
+def test_reduce_random_partials(dev, S):
+    log(f"[reduce S={S}]")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(500 + S)
+    rows, D = 37, 128
+    po = torch.randn((rows, S, D), generator=g, dtype=torch.float32)
+    pl = torch.randn((rows, S), generator=g, dtype=torch.float32) * 20
+    drop = torch.rand((rows, S), generator=g) < 0.3
+    pl[drop] = -math.inf
+    pl[3] = -math.inf  # a row with every split empty
+    ref, ref_lse = oracle.merge(po.double().numpy(), pl.double().numpy())
+    for dt in (torch.float32, torch.bfloat16):
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+        out = pa.splitkv_reduce(po.to(dev), pl.to(dev), out_dtype=dt, lse=lse)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        tol = 2e-3 if dt == torch.float32 else 2e-2  # |O| reaches ~4 here
+        assert np.max(np.abs(got - ref)) <= tol
+        gl = lse.cpu().numpy()
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(gl))
+        assert np.max(np.abs(gl[fin] - ref_lse[fin])) <= LSE_TOL
+        assert np.all(got[3] == 0)
+
+
+# ------------------------------------------------------- named workloads ----
+
+def _sample_rows(b, n, seed):
+    T, Hq = b.q.shape[:2]
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T * Hq, size=min(n, T * Hq), replace=False).tolist())
+    # always include the first and last token of every sequence, all heads
+    if b.query_start_loc is not None:
+        qsl = b.query_start_loc.cpu().tolist()
+        for s in range(b.num_seqs):
+            for t in {qsl[s], qsl[s + 1] - 1}:
+                if qsl[s + 1] > qsl[s]:
+                    rows.update(t * Hq + h for h in range(Hq))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
+def test_named_workload(dev, name):
+    """Each workload at full size, launched as the benchmark launches it."""
+    log(f"[workload {name}]")
+    spec = workloads.WORKLOADS[name]
+    b = workloads.generate(spec, dev, fill="nan")
+    if spec.decode_layout:
+        out, lse = run_decode(b, torch.bfloat16)
+        rows = None
+    else:
+        out, lse = run_prefill(b, torch.bfloat16)
+        rows = _sample_rows(b, 3000, seed=1)
+        if name == "mixed_unified":  # every decode row too
+            dec = np.arange(16 * 32, dtype=np.int64)
+            rows = np.union1d(rows, dec)
+    compare(b, out, lse, rows=rows, label=f"workload {name}")
+    if name == "decode_ctx512":
+        out32, lse32 = run_decode(b, torch.float32)
+        compare(b, out32, lse32, label="workload decode_ctx512 fp32")
