@@ -32,6 +32,15 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 DECODE_BYTES_PER_TOKEN = 4096
 
+# HBM bytes per decode launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
+# (scaled by a plain copy of known size), for the kernel as last profiled;
+# None until counters are taken for the current kernel.
+TRAFFIC = {
+    # decode_kernel<4,4,false> + splitkv_reduce_kernel, num_splits 32
+    # (profiles/decode_ctx32k_hbm_counters.md)
+    "decode_ctx32k": 135690857,
+}
+
 
 def note(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -40,12 +49,19 @@ def note(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_ctx32k")
     ap.add_argument("--pools", type=int, default=6, help="K/V pool copies cycled over steps")
     ap.add_argument("--splits", type=int, default=0, help="force num_splits (0 = table)")
+    ap.add_argument("--waves", type=int, default=0, help="force waves per workgroup (0 = table)")
+    ap.add_argument("--variant", type=int, default=-1, help="force pa_tiles.variant (-1 = table)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill workload (profiling runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run 4 plain device copies of MIB MiB (a known-size "
+                         "kernel for scaling HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
@@ -65,20 +81,27 @@ def prefill_flops(b):
     return 4 * D * Hq * total
 
 
-def time_replays(torch, graphs, steps, warmup):
-    """Replay graphs round-robin; events around every replay on the replay
-    stream.  Returns (total ms, per-replay ms list)."""
+def time_replays(torch, graph_all, singles, steps, warmup):
+    """Time exactly `steps` steps: replays of graph_all (one step per pool
+    copy, len(singles) steps each), then single-step graphs for the rest.
+    HIP events on the replay stream bracket every replay.  Returns
+    (total ms, ms per step of each replay)."""
+    per_all = len(singles)
     for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+        singles[i % per_all].replay()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    plan = [(graph_all, per_all)] * (steps // per_all)
+    plan += [(singles[i], 1) for i in range(steps % per_all)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
     torch.cuda.synchronize()
     evs[0].record()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    for i, (g, _) in enumerate(plan):
+        g.replay()
         evs[i + 1].record()
     torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    per = []
+    for i, (_, n) in enumerate(plan):
+        per += [evs[i].elapsed_time(evs[i + 1]) / n] * n
     return evs[0].elapsed_time(evs[-1]), per
 
 
@@ -94,10 +117,12 @@ def bench_decode(torch, pa, workloads, args, dev):
     max_ctx = b.max_context_len  # host bound, read once outside any capture
     problem = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale, max_ctx, 1)
     tiles, ws = pa.select_tiles(problem)
-    if args.splits:
-        tiles.num_splits = args.splits
+    if args.splits or args.waves or args.variant >= 0:
+        tiles.num_splits = args.splits or tiles.num_splits
+        tiles.waves_per_wg = args.waves or tiles.waves_per_wg
+        tiles.variant = args.variant if args.variant >= 0 else tiles.variant
         ws = pa.workspace_size(problem, tiles)
-    workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)  # counters start at 0
     out = torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)
 
     def step(kp, vp):
@@ -107,15 +132,19 @@ def bench_decode(torch, pa, workloads, args, dev):
     for kp, vp in pools:  # eager warm-up (and first-launch costs) outside capture
         step(kp, vp)
     torch.cuda.synchronize()
-    graphs = []
+    singles = []
     for kp, vp in pools:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(kp, vp)
-        graphs.append(g)
+        singles.append(g)
+    g_all = torch.cuda.CUDAGraph()  # one decode step per pool copy, back to back
+    with torch.cuda.graph(g_all):
+        for kp, vp in pools:
+            step(kp, vp)
     torch.cuda.synchronize()
-    note(f"captured {len(graphs)} decode graphs, tiles={tiles.as_dict()}")
-    total_ms, per = time_replays(torch, graphs, args.steps, args.warmup)
+    note(f"captured decode graphs ({len(pools)} steps per replay), tiles={tiles.as_dict()}")
+    total_ms, per = time_replays(torch, g_all, singles, args.steps, args.warmup)
     nbytes = decode_bytes(b)
     return dict(batch=b, tiles=tiles, total_ms=total_ms, per=per, nbytes=nbytes,
                 pool_bytes=sum(p[0].numel() * 2 * 2 for p in pools))
@@ -128,7 +157,7 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup):
     problem = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
                               max_ctx, max_q, causal=spec.causal)
     tiles, ws = pa.select_tiles(problem)
-    workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
     out = torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)
 
     def step():
@@ -141,7 +170,7 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    total_ms, per = time_replays(torch, [g], steps, warmup)
+    total_ms, per = time_replays(torch, g, [g], steps, warmup)
     flops = prefill_flops(b)
     avg_ms = sum(per) / len(per)
     tfs = flops / (avg_ms * 1e-3) / 1e12
@@ -152,6 +181,19 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup):
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None}}
+
+
+def calibrate_copy(torch, dev, mib):
+    """Plain device-to-device copies of a known size (for counter scaling)."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    note(f"calibration: 4 copies of {mib} MiB")
 
 
 def cpu_baseline(workloads, b, seconds):
@@ -194,6 +236,12 @@ def main():
     pa.load()
     dev = torch.device("cuda:0")
 
+    if args.prefill_only:
+        pre = bench_prefill(torch, pa, workloads, dev, args.steps, args.warmup)
+        note(f"prefill: {pre['value']} TFLOP/s")
+        calibrate_copy(torch, dev, args.calibrate_copy)
+        print(json.dumps(pre), flush=True)
+        return
     d = bench_decode(torch, pa, workloads, args, dev)
     b = d["batch"]
     ms_per_step = d["total_ms"] / args.steps
@@ -220,9 +268,11 @@ def main():
                         f"{b.max_context_len}, 32 q / 8 kv heads, head_dim 128, page 16, "
                         f"pool {b.spec.pool_pages} pages",
             "num_splits": d["tiles"].num_splits,
+            "waves_per_wg": d["tiles"].waves_per_wg,
+            "variant": d["tiles"].variant,
             "pool_copies": args.pools,
             "kv_bytes_per_step": d["nbytes"],
-            "graph": "hipGraph replay",
+            "graph": "hipGraph replays, one decode step per pool copy in each",
         },
         "roofline": {
             "bound": "hbm",
@@ -230,7 +280,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": TRAFFIC.get(args.workload),
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
         },
     }
@@ -241,6 +291,7 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(workloads, b, args.cpu_seconds)
         note(f"cpu baseline: {result['cpu_baseline']}")
+    calibrate_copy(torch, dev, args.calibrate_copy)
     print(json.dumps(result), flush=True)
 
 

@@ -100,7 +100,10 @@ typedef struct pa_tiles {
   int32_t q_tokens_per_tile; /* query tokens per prefill workgroup               */
   int32_t variant;           /* bit 0 (prefill): carry P as a bf16 high part plus a  */
                              /* bf16 remainder in P.V (relative weight error ~2^-18  */
-                             /* instead of ~2^-9); chosen for fp32 outputs           */
+                             /* instead of ~2^-9); chosen for fp32 outputs.          */
+                             /* bit 1 (decode, S > 1): merge the splits in a second  */
+                             /* kernel (pa_splitkv_reduce's) instead of in the last  */
+                             /* workgroup of each sequence                           */
 } pa_tiles;
 
 /* Pick the launch shape for a problem from the built-in table (the offline
@@ -119,10 +122,17 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
  * each sequence is cut into S contiguous, page-aligned ranges processed by
  * different workgroups; their (normalised output, lse) partials go to the
  * workspace and are merged by log-sum-exp in the same call.
+ * The merge runs inside the same launch: the last workgroup of a (sequence,
+ * kv head) to finish, found with an atomic arrival counter, merges that
+ * sequence's partials, so one decode call is one kernel.
  * q: bf16 [B, Hq, D]; out: [B, Hq, D] of problem->out_dtype; lse: fp32
  * [B, Hq] or NULL.  workspace: >= pa_workspace_size bytes, 256-byte aligned,
- * may be NULL when that size is 0.  Pointers to bf16 data must be 16-byte
- * aligned. */
+ * may be NULL when that size is 0.  It holds the partials and the arrival
+ * counters: it must be zero-filled before its first use, and every call
+ * leaves the counters zero again, so it can be reused (and captured) without
+ * clearing.  Calls that share one workspace must not run concurrently.
+ * tiles->waves_per_wg is 4 or 8 (4 when G = 16).  Pointers to bf16 data must
+ * be 16-byte aligned. */
 pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void* q,
                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
                     const int32_t* context_lens, void* out, float* lse, void* workspace,
@@ -149,7 +159,8 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
  *   every lse_k = -inf gives out[r] = 0 and lse_out[r] = -inf.
  * partial_o: fp32 [rows, S, head_dim] (normalised per split); partial_lse:
  * fp32 [rows, S]; out: [rows, head_dim] of out_dtype; lse_out: fp32 [rows]
- * or NULL.  head_dim must be a positive multiple of 4 (at most 1024). */
+ * or NULL.  head_dim must be a positive multiple of 4 (at most 1024),
+ * 1 <= num_splits <= 4096; partial_o and out 16-byte aligned. */
 pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, int32_t rows,
                             int32_t num_splits, int32_t head_dim, void* out,
                             pa_dtype out_dtype, float* lse_out, hipStream_t stream);

@@ -49,10 +49,22 @@ pa_status check_tiles(const pa_tiles* t) {
   return PA_OK;
 }
 
-size_t partial_bytes(int64_t rows, int splits, int head_dim) {
-  if (splits <= 1) return 0;
-  return align_up((size_t)rows * splits * head_dim * sizeof(float)) +
-         align_up((size_t)rows * splits * sizeof(float));
+// Decode workspace: partial O [rows, S, D] fp32, partial lse [rows, S] fp32,
+// and one int32 arrival counter per (sequence, kv head); 256-byte aligned
+// regions.  The counters must be zero before the first call; every call
+// leaves them zero.
+struct DecodeWorkspace {
+  size_t o_off, lse_off, ctr_off, total;
+};
+
+DecodeWorkspace decode_workspace(int64_t rows, int splits, int head_dim, int64_t counters) {
+  DecodeWorkspace w{0, 0, 0, 0};
+  if (splits <= 1) return w;
+  w.o_off = 0;
+  w.lse_off = align_up((size_t)rows * splits * head_dim * sizeof(float));
+  w.ctr_off = w.lse_off + align_up((size_t)rows * splits * sizeof(float));
+  w.total = w.ctr_off + align_up((size_t)counters * sizeof(int32_t));
+  return w;
 }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -81,7 +93,9 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
   const int64_t rows = (int64_t)problem->max_query_len <= 1
                            ? (int64_t)problem->num_seqs * problem->num_q_heads
                            : (int64_t)problem->total_query_tokens * problem->num_q_heads;
-  *workspace_bytes = partial_bytes(rows, tiles->num_splits, problem->head_dim);
+  *workspace_bytes = decode_workspace(rows, tiles->num_splits, problem->head_dim,
+                                      (int64_t)problem->num_seqs * problem->num_kv_heads)
+                         .total;
   return PA_OK;
 }
 
@@ -94,10 +108,13 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
   memset(&t, 0, sizeof t);
   if (problem->max_query_len <= 1) {
     t.kv_tile = pa::kDecodeTile;
-    t.waves_per_wg = 4;
+    t.waves_per_wg = pa::table_decode_waves(problem->num_seqs, problem->num_kv_heads,
+                                            problem->max_context_len, G);
     t.q_tokens_per_tile = 1;
     t.num_splits = pa::table_decode_splits(problem->num_seqs, problem->num_kv_heads,
                                            problem->max_context_len);
+    t.variant = pa::table_decode_variant(problem->num_seqs, problem->num_kv_heads,
+                                         problem->max_context_len);
   } else {
     t.kv_tile = 32;
     t.waves_per_wg = 4;
@@ -122,14 +139,18 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PA_ERR_INVALID_ARG;
   const int S = tiles->num_splits;
+  const int G = problem->num_q_heads / problem->num_kv_heads;
+  const int waves = tiles->waves_per_wg;
+  if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
+  if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)problem->num_seqs * problem->num_q_heads;
-  const size_t need = partial_bytes(rows, S, problem->head_dim);
-  if (need > 0 && (!workspace || workspace_bytes < need ||
-                   (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+  const DecodeWorkspace wl = decode_workspace(rows, S, problem->head_dim,
+                                              (int64_t)problem->num_seqs * problem->num_kv_heads);
+  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total ||
+                       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0) return PA_OK;
 
-  const int G = problem->num_q_heads / problem->num_kv_heads;
   const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
   pa::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -141,10 +162,12 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   p.lse = lse;
   p.part_o = nullptr;
   p.part_lse = nullptr;
+  p.counters = nullptr;
   if (S > 1) {
-    p.part_o = static_cast<float*>(workspace);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align_up((size_t)rows * S * problem->head_dim * sizeof(float)));
+    char* ws = static_cast<char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    p.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+    p.counters = reinterpret_cast<int32_t*>(ws + wl.ctr_off);
   }
   p.stride_page = problem->kv_stride_page;
   p.stride_token = problem->kv_stride_token;
@@ -157,8 +180,9 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   p.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
   p.scale_log2 = problem->scale * pa::kLog2eHost;
   p.out_f32 = problem->out_dtype == PA_FP32;
-  if ((st = from_hip(pa::launch_decode(p, G, stream))) != PA_OK) return st;
-  if (S > 1) {
+  const bool separate = S > 1 && (tiles->variant & pa::kVariantSeparateMerge) != 0;
+  if ((st = from_hip(pa::launch_decode(p, G, waves, !separate, stream))) != PA_OK) return st;
+  if (separate) {
     pa::ReduceParams r;
     r.part_o = p.part_o;
     r.part_lse = p.part_lse;
@@ -168,9 +192,9 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
     r.num_splits = S;
     r.head_dim = problem->head_dim;
     r.out_f32 = p.out_f32;
-    if ((st = from_hip(pa::launch_reduce(r, stream))) != PA_OK) return st;
+    st = from_hip(pa::launch_reduce(r, stream));
   }
-  return PA_OK;
+  return st;
 }
 
 pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const void* q,
@@ -221,7 +245,8 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
 pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, int32_t rows,
                             int32_t num_splits, int32_t head_dim, void* out,
                             pa_dtype out_dtype, float* lse_out, hipStream_t stream) {
-  if (rows < 0 || num_splits < 1 || head_dim <= 0 || head_dim % 4 != 0 || head_dim > 1024)
+  if (rows < 0 || num_splits < 1 || num_splits > pa::kReduceMaxSplits || head_dim <= 0 ||
+      head_dim % 4 != 0 || head_dim > 1024)
     return PA_ERR_INVALID_ARG;
   if (out_dtype != PA_BF16 && out_dtype != PA_FP32) return PA_ERR_INVALID_ARG;
   if (rows == 0) return PA_OK;

@@ -9,11 +9,13 @@ namespace pa {
 constexpr int kHeadDim = 128;   // built head dimension
 constexpr int kPage = 16;       // built page size
 constexpr int kDecodeTile = 16; // keys per decode step (one MFMA N-tile)
-constexpr int kMaxSplits = 256;
+constexpr int kMaxSplits = 256;        // decode split-KV
+constexpr int kReduceMaxSplits = 4096; // pa_splitkv_reduce
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 // pa_tiles.variant bits
-constexpr int kVariantPreciseP = 1;  // prefill: P as bf16 high + remainder
+constexpr int kVariantPreciseP = 1;      // prefill: P as bf16 high + remainder
+constexpr int kVariantSeparateMerge = 2; // decode: merge splits in a second kernel
 
 struct DecodeParams {
   const uint16_t* q;        // [B, Hq, D] bf16
@@ -25,6 +27,7 @@ struct DecodeParams {
   float* lse;               // [B, Hq] or null
   float* part_o;            // [B*Hq, S, D] when S > 1
   float* part_lse;          // [B*Hq, S]
+  int32_t* counters;        // [B*Hkv] split arrival counters, zero between calls
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
   int32_t tiles_per_split;  // 16-key tiles per split
@@ -59,7 +62,8 @@ struct ReduceParams {
 };
 
 // Launchers: return hipSuccess or the launch error.  Shapes were checked.
-hipError_t launch_decode(const DecodeParams& p, int group, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int group, int waves, bool fused,
+                         hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int group, int grid_x, bool precise_p,
                           hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);

@@ -172,7 +172,10 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
            out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
            tiles: Optional[Tiles] = None, workspace: Optional[torch.Tensor] = None,
            problem: Optional[Problem] = None) -> torch.Tensor:
-    """pa_decode: q [B, Hq, D] bf16 (one query token per sequence)."""
+    """pa_decode: q [B, Hq, D] bf16 (one query token per sequence).
+
+    A caller-provided workspace must have been zero-filled once (its split
+    counters); every call leaves it reusable."""
     lib = load()
     B = q.shape[0]
     if out is None:
@@ -188,7 +191,7 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     else:
         ws = workspace_size(problem, tiles)
     if ws and workspace is None:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=q.device)  # counters start at 0
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pa_decode(ctypes.byref(problem), ctypes.byref(tiles), _ptr(q), _ptr(k_pool),
                          _ptr(v_pool), _ptr(block_tables), _ptr(context_lens), _ptr(out),
@@ -223,7 +226,7 @@ def prefill(q: torch.Tensor, query_start_loc: torch.Tensor, k_pool: torch.Tensor
     else:
         ws = workspace_size(problem, tiles)
     if ws and workspace is None:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pa_prefill(ctypes.byref(problem), ctypes.byref(tiles), _ptr(q),
                           _ptr(query_start_loc), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),

@@ -36,16 +36,23 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_decode(b, out_dtype=torch.bfloat16, splits=None, with_lse=True):
+def run_decode(b, out_dtype=torch.bfloat16, splits=None, with_lse=True, waves=None,
+               workspace=None, variant=None):
     lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=b.q.device) if with_lse else None
     tiles = None
-    if splits is not None:
+    if splits is not None or waves is not None or variant is not None:
         pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, b.spec.scale,
                              b.max_context_len, 1, out_dtype=out_dtype)
         tiles, _ = pa.select_tiles(pb)
-        tiles.num_splits = splits
+        if splits is not None:
+            tiles.num_splits = splits
+        if waves is not None:
+            tiles.waves_per_wg = waves
+        if variant is not None:
+            tiles.variant = variant
     out = pa.decode(b.q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, b.spec.scale,
-                    b.max_context_len, out_dtype=out_dtype, lse=lse, tiles=tiles)
+                    b.max_context_len, out_dtype=out_dtype, lse=lse, tiles=tiles,
+                    workspace=workspace)
     torch.cuda.synchronize()
     return out, lse
 
@@ -105,14 +112,40 @@ DECODE_CASES = [
 
 @pytest.mark.parametrize("name,ctx,hq,hkv", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
 @pytest.mark.parametrize("splits", [None, 1, 3, 64])
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("merge", ["fused", "separate"])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_decode_small(dev, name, ctx, hq, hkv, splits, out_dtype):
-    log(f"[decode {name} splits={splits} {out_dtype}]")
+def test_decode_small(dev, name, ctx, hq, hkv, splits, waves, merge, out_dtype):
+    if hq // hkv == 16 and waves == 8:
+        pytest.skip("G = 16 is built with 4 waves per workgroup only")
+    log(f"[decode {name} splits={splits} waves={waves} {merge} {out_dtype}]")
     spec = workloads.small_spec(f"dec_{name}", seed=100 + len(ctx) + hq, contexts=ctx,
                                 queries=[1] * len(ctx), num_q_heads=hq, num_kv_heads=hkv)
     b = workloads.generate(spec, dev)
-    out, lse = run_decode(b, out_dtype, splits)
-    compare(b, out, lse, label=f"decode {name} S={splits}")
+    out, lse = run_decode(b, out_dtype, splits, waves=waves,
+                          variant=2 if merge == "separate" else 0)
+    compare(b, out, lse, label=f"decode {name} S={splits} W={waves} {merge}")
+
+
+def test_decode_workspace_reuse(dev):
+    """One zero-filled workspace serves many calls: the merge counters reset."""
+    log("[decode workspace reuse]")
+    spec = workloads.small_spec("reuse", seed=9, contexts=[3000, 40, 1200], queries=[1, 1, 1])
+    b = workloads.generate(spec, dev)
+    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                         b.max_context_len, 1)
+    t, _ = pa.select_tiles(pb)
+    t.num_splits = 64  # the largest split count used below
+    ws = torch.zeros(pa.workspace_size(pb, t), dtype=torch.uint8, device=dev)
+    first = None
+    for S in (16, 16, 5, 64, 16):
+        out, lse = run_decode(b, torch.float32, S, workspace=ws)
+        compare(b, out, lse, label=f"reuse S={S}")
+        if S == 16:
+            if first is None:
+                first = out.clone()
+            else:
+                assert torch.equal(out, first), "same call, different bits"
 
 
 def test_decode_logit_stress(dev):
