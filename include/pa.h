@@ -88,7 +88,7 @@ typedef struct pa_problem {
   int32_t max_query_len;      /* bound on every query length; 1 for decode      */
   int32_t total_query_tokens; /* T: rows of q and out                           */
   int32_t causal;             /* 0 or 1 (decode rows are unaffected)            */
-  float scale;                /* multiplies q.k; e.g. 1/sqrt(D)                 */
+  float scale;                /* multiplies q.k, finite and > 0; e.g. 1/sqrt(D)  */
   pa_dtype out_dtype;         /* PA_BF16 or PA_FP32                             */
 } pa_problem;
 

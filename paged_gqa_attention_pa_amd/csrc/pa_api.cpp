@@ -35,7 +35,7 @@ pa_status check_problem(const pa_problem* pb) {
     return PA_ERR_INVALID_ARG;
   if (pb->out_dtype != PA_BF16 && pb->out_dtype != PA_FP32) return PA_ERR_INVALID_ARG;
   if (pb->causal != 0 && pb->causal != 1) return PA_ERR_INVALID_ARG;
-  if (!(pb->scale == pb->scale)) return PA_ERR_INVALID_ARG;  // NaN scale
+  if (!(pb->scale > 0.f) || pb->scale == __builtin_inff()) return PA_ERR_INVALID_ARG;
   if ((int64_t)pb->max_context_len > (int64_t)pb->max_blocks_per_seq * pb->page_size)
     return PA_ERR_INVALID_ARG;
   if (pb->head_dim != kHeadDim || pb->page_size != kPage) return PA_ERR_UNSUPPORTED;
@@ -117,8 +117,8 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
                                          problem->max_context_len);
   } else {
     t.kv_tile = 32;
-    t.waves_per_wg = 4;
-    t.q_tokens_per_tile = 128 / G;
+    t.waves_per_wg = 8;
+    t.q_tokens_per_tile = 256 / G;
     t.num_splits = 1;
     // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18
     t.variant = problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0;
@@ -214,7 +214,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     return PA_ERR_INVALID_ARG;
   if (problem->num_seqs == 0 || problem->total_query_tokens == 0) return PA_OK;
   const int G = problem->num_q_heads / problem->num_kv_heads;
-  const int qt = 128 / G;
+  const int qt = 256 / G;
   pa::PrefillParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.query_start_loc = query_start_loc;

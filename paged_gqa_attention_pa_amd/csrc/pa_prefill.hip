@@ -1,12 +1,12 @@
 // Paged GQA prefill / chunked prefill / mixed batch for gfx950 (bf16 MFMA).
 //
 // One workgroup = (query tile of one sequence, kv head).  Its Q-block is
-// 128 rows: QT = 128 / G query tokens x the G query heads that share the KV
+// 256 rows: QT = 256 / G query tokens x the G query heads that share the KV
 // head (the Q-Block step of the IBM Triton summary's five-step list), row
 // r -> token r / G, head r % G; wavefront w owns rows 32w..32w+31 and each
 // lane owns one row (lane % 32).  The workgroup walks the sequence's keys in
 // tiles of 32 (two pages), up to the causal limit of its last token, staging
-// each K and V tile in LDS once for all four wavefronts (FlashAttention-style
+// each K and V tile in LDS once for all eight wavefronts (FlashAttention-style
 // tiling, guide sections "Flash Attention革命" and "Triton实现Flash
 // Attention"):
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, K rows from LDS (16-byte reads),
@@ -31,10 +31,13 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;   // Q-block rows per workgroup
 constexpr int kKvTile = 32;          // keys per inner step
-constexpr int kLdsStride = kHeadDim + 8;  // bf16 elements per LDS row (272 B)
+constexpr int kLdsStride = kHeadDim + 8;  // K: bf16 elements per LDS row (272 B)
+constexpr int kVtStride = kKvTile + 4;    // V^T: bf16 elements per LDS row (72 B)
+constexpr int kBufs = 3;                  // LDS tile buffers
 constexpr float kLazyThreshold = 8.0f;
 
 // Find (sequence, query tile) of workgroup x: tiles are numbered sequence by
@@ -79,12 +82,18 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, int* 
 }
 
 template <int G, bool PRECISE>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, int nx) {
   constexpr int D = kHeadDim;
   constexpr int QT = kRows / G;
-  const int g = blockIdx.y;
+  // 1-D grid: id -> (kv head, query tile).  Consecutive ids go to different
+  // XCDs, so with Hkv = 8 each XCD serves one KV head and its K/V stay in
+  // that XCD's L2.  Query tiles run from the last (heaviest under the causal
+  // mask) to the first.
+  const int id = blockIdx.x;
+  const int g = id % p.num_kv_heads;
+  const int x = nx - 1 - id / p.num_kv_heads;
   int s, qtile;
-  if (!find_tile(p.query_start_loc, p.num_seqs, QT, blockIdx.x, &s, &qtile)) return;
+  if (!find_tile(p.query_start_loc, p.num_seqs, QT, x, &s, &qtile)) return;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -95,12 +104,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   const int tok0 = qtile * QT;
   const int ntok = min(QT, qlen - tok0);
 
-  // This lane's row.
+  // This lane's row: token r / G, head r % G.
   const int r = 32 * wave + n;
   const int tl = r / G, h = r % G;
   const bool row_valid = tl < ntok;
   const int qi = tok0 + tl;  // index of the token inside the chunk
   const int key_limit = p.causal ? min(L, L - qlen + qi + 1) : L;  // keys < limit
+  // smallest limit among this wave's rows (its first token): tiles that end
+  // below it need no mask
+  const int wave_limit = p.causal ? min(L, L - qlen + tok0 + (32 * wave) / G + 1) : L;
   const int kv_end = p.causal ? min(L, L - qlen + tok0 + ntok) : L;
   const int nkv = kv_end > 0 ? (kv_end + kKvTile - 1) / kKvTile : 0;
 
@@ -113,38 +125,58 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
       qb[ks] = row_valid ? as_bf16x8(ld16(qrow + 16 * ks)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKvTile * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kKvTile * kLdsStride];
+  // LDS, three buffers: K row-major [key][dim] (272-byte rows), V transposed
+  // [dim][key] (72-byte rows: 32 keys + pad), so both MFMA operands are plain
+  // 16- and 8-byte LDS reads.  While tile j is being finished (softmax, P.V),
+  // the S^T MFMAs of tile j+1 already run and tile j+2 is being stored: one
+  // barrier per tile.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBufs][kKvTile * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kBufs][D * kVtStride];
 
-  // Tile loader: 32 keys x 16 chunks of 16 bytes, two chunks per thread.
+  // Tile loader: threads 0..255 stage K, threads 256..511 stage V; thread t
+  // (mod 256) handles keys 2*(t%16), 2*(t%16)+1 (same page) and dims
+  // 8*((t%256)/16) .. +7.
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
-  const uint16_t* kb = p.k_pool + (int64_t)g * p.stride_head;
-  const uint16_t* vb = p.v_pool + (int64_t)g * p.stride_head;
-  uint4 kreg[2], vreg[2];
+  const bool v_side = tid >= 256;
+  const uint16_t* src = (v_side ? p.v_pool : p.k_pool) + (int64_t)g * p.stride_head;
+  const int kp = tid & 15, dc = (tid & 255) >> 4;
+  uint4 reg[2];
   auto load_tile = [&](int j) {
+    const int key = j * kKvTile + 2 * kp;
+    const int64_t page = key < L ? bt[key / kPage] : 0;
+    const int64_t off = page * p.stride_page + (int64_t)(key % kPage) * p.stride_token + 8 * dc;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    reg[0] = key < L ? ld16(src + off) : z;
+    reg[1] = key + 1 < L ? ld16(src + off + p.stride_token) : z;
+  };
+  auto store_tile = [&](int buf) {
+    if (!v_side) {
+      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp) * kLdsStride + 8 * dc]) = reg[0];
+      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp + 1) * kLdsStride + 8 * dc]) = reg[1];
+    } else {
+      const uint32_t a[4] = {reg[0].x, reg[0].y, reg[0].z, reg[0].w};
+      const uint32_t b[4] = {reg[1].x, reg[1].y, reg[1].z, reg[1].w};
+      uint32_t* vt = reinterpret_cast<uint32_t*>(&vt_lds[buf][0]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int id = tid + 256 * u;
-      const int key = j * kKvTile + (id >> 4);
-      const int col = (id & 15) * 8;
-      if (key < L) {
-        const int64_t page = bt[key / kPage];
-        const int64_t off = page * p.stride_page + (int64_t)(key % kPage) * p.stride_token + col;
-        kreg[u] = ld16(kb + off);
-        vreg[u] = ld16(vb + off);
-      } else {
-        kreg[u] = make_uint4(0, 0, 0, 0);
-        vreg[u] = make_uint4(0, 0, 0, 0);
+      for (int w = 0; w < 4; ++w) {
+        // dims 8dc+2w and 8dc+2w+1: (key 2kp, key 2kp+1) pairs
+        vt[((8 * dc + 2 * w) * kVtStride + 2 * kp) / 2] = (a[w] & 0xffffu) | (b[w] << 16);
+        vt[((8 * dc + 2 * w + 1) * kVtStride + 2 * kp) / 2] = (a[w] >> 16) | (b[w] & 0xffff0000u);
       }
     }
   };
-  auto store_tile = [&]() {
+  // S^T = K Q^T for the tile in buffer buf, D = 128 in 8 steps of 16.
+  auto qk = [&](int buf, f32x16& st) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int id = tid + 256 * u;
-      const int idx = (id >> 4) * kLdsStride + (id & 15) * 8;
-      *reinterpret_cast<uint4*>(&k_lds[idx]) = kreg[u];
-      *reinterpret_cast<uint4*>(&v_lds[idx]) = vreg[u];
+    for (int e = 0; e < 16; ++e) st[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      // two 8-byte LDS reads: measured faster than one 16-byte read on gfx950
+      const uint16_t* kr = &k_lds[buf][n * kLdsStride + 16 * ks + 8 * half];
+      const uint2 a0 = *reinterpret_cast<const uint2*>(kr);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(kr + 4);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)), qb[ks], st, 0, 0, 0);
     }
   };
 
@@ -154,35 +186,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[mt][e] = 0.f;
   float m = kNegInf, lsum = 0.f;
+  const float c = p.scale_log2;  // > 0 (checked on the host)
 
-  if (nkv > 0) load_tile(0);
+#pragma unroll
+  for (int j = 0; j < kBufs - 1; ++j)
+    if (j < nkv) {
+      load_tile(j);
+      store_tile(j);
+    }
+  __syncthreads();
+  if (kBufs - 1 < nkv) load_tile(kBufs - 1);
+  f32x16 st_cur, st_next;
+  if (nkv > 0) qk(0, st_cur);
+
   for (int j = 0; j < nkv; ++j) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (j + 1 < nkv) load_tile(j + 1);
+    const int buf = j % kBufs;
+    if (j + 1 < nkv) qk((j + 1) % kBufs, st_next);  // MFMA pipe, overlaps the softmax below
 
-    // S^T = K Q^T over D = 128 (8 steps of 16).
-    f32x16 st;
+    // Register e holds key 8*(e/4) + 4*half + e%4 of tile j, row n; the
+    // log2-domain logit is c*S (c > 0, so the max can be taken on S).
+    float smax = kNegInf;
+    const bool full = j * kKvTile + kKvTile <= wave_limit;  // no key of the tile masked
+    if (!full) {
+      const int kbase = j * kKvTile + 4 * half;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) st[e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[n * kLdsStride + 16 * ks + 8 * half]);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[ks], st, 0, 0, 0);
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + (e & 3);
+        st_cur[e] = (key < key_limit) ? st_cur[e] : kNegInf;
+      }
     }
-
-    // Register e holds key 8*(e/4) + 4*half + e%4 of this tile, row n.
-    const int kbase = j * kKvTile + 4 * half;
-    float x[16];
-    float tmax = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kbase + 8 * (e >> 2) + (e & 3);
-      x[e] = (key < key_limit) ? st[e] * p.scale_log2 : kNegInf;
-      tmax = fmaxf(tmax, x[e]);
-    }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, st_cur[e]);
+    const float tmax = fmaxf(smax, shfl_xor(smax, 32)) * c;
     const bool need = tmax > m + kLazyThreshold;
     if (wave_any(need)) {
       const float m_new = need ? tmax : m;
@@ -194,13 +229,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[mt][e] *= alpha;
     }
-    const float m_use = (m == kNegInf) ? 0.f : m;
+    const float neg_m = (m == kNegInf) ? 0.f : -m;
     uint32_t pk[8], pl[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
-      const float p0 = fast_exp2(x[e] - m_use);
-      const float p1 = fast_exp2(x[e + 1] - m_use);
+      const float p0 = fast_exp2(fmaf(st_cur[e], c, neg_m));
+      const float p1 = fast_exp2(fmaf(st_cur[e + 1], c, neg_m));
       psum += p0 + p1;
       pk[e >> 1] = pack_bf16x2(p0, p1);
       if constexpr (PRECISE) {
@@ -210,6 +245,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     lsum += psum;
 
     // O^T += V^T P^T: two k-steps of 16 keys, four 32-dim M tiles.
+    const uint16_t* vt = &vt_lds[buf][0];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * kk], pk[4 * kk + 1],
@@ -220,22 +256,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                                                     pl[4 * kk + 3]));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int d = 32 * mt + n;
-        uint16_t vv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = 16 * kk + 8 * (i >> 2) + 4 * half + (i & 3);
-          vv[i] = v_lds[key * kLdsStride + d];
-        }
-        const uint4 va = make_uint4((uint32_t)vv[0] | ((uint32_t)vv[1] << 16),
-                                    (uint32_t)vv[2] | ((uint32_t)vv[3] << 16),
-                                    (uint32_t)vv[4] | ((uint32_t)vv[5] << 16),
-                                    (uint32_t)vv[6] | ((uint32_t)vv[7] << 16));
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pb, o[mt], 0, 0, 0);
+        const uint16_t* row = vt + (32 * mt + n) * kVtStride + 16 * kk + 4 * half;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row);      // keys +0..3
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 8);  // keys +8..11
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[mt], 0, 0, 0);
         if constexpr (PRECISE)
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pbl, o[mt], 0, 0, 0);
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbl, o[mt], 0, 0, 0);
       }
     }
+    // Tile j+2 goes to the buffer tile j-1 used (its last reads were before
+    // the previous barrier); its global loads were issued an iteration ago.
+    if (j + kBufs - 1 < nkv) store_tile((j + kBufs - 1) % kBufs);
+    __syncthreads();
+    if (j + kBufs < nkv) load_tile(j + kBufs);
+    st_cur = st_next;
   }
 
   const float l = lsum + shfl_xor(lsum, 32);
@@ -263,14 +298,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 }  // namespace
 
 template <bool PRECISE>
-hipError_t launch_prefill_t(const PrefillParams& p, int group, dim3 grid, hipStream_t stream) {
-  dim3 block(256);
+hipError_t launch_prefill_t(const PrefillParams& p, int group, int nx, hipStream_t stream) {
+  const dim3 grid((unsigned)nx * (unsigned)p.num_kv_heads);
+  const dim3 block(kThreads);
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<1, PRECISE>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<2, PRECISE>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<4, PRECISE>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<8, PRECISE>), grid, block, 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<16, PRECISE>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<1, PRECISE>), grid, block, 0, stream, p, nx); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<2, PRECISE>), grid, block, 0, stream, p, nx); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<4, PRECISE>), grid, block, 0, stream, p, nx); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<8, PRECISE>), grid, block, 0, stream, p, nx); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<16, PRECISE>), grid, block, 0, stream, p, nx); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -279,9 +315,9 @@ hipError_t launch_prefill_t(const PrefillParams& p, int group, dim3 grid, hipStr
 hipError_t launch_prefill(const PrefillParams& p, int group, int grid_x, bool precise_p,
                           hipStream_t stream) {
   if (grid_x <= 0) return hipSuccess;
-  dim3 grid(grid_x, p.num_kv_heads, 1);
-  return precise_p ? launch_prefill_t<true>(p, group, grid, stream)
-                   : launch_prefill_t<false>(p, group, grid, stream);
+  if ((int64_t)grid_x * p.num_kv_heads > 0x7fffffff) return hipErrorInvalidValue;
+  return precise_p ? launch_prefill_t<true>(p, group, grid_x, stream)
+                   : launch_prefill_t<false>(p, group, grid_x, stream);
 }
 
 }  // namespace pa

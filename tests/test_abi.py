@@ -63,7 +63,7 @@ def test_select_tiles_decode_and_prefill(lib):
     assert st == pa.PA_OK and t.num_splits > 8 and ws > 0
     st, t, ws = _select(lib, _problem(max_query_len=2048, total_query_tokens=8192,
                                       max_context_len=3072))
-    assert st == pa.PA_OK and t.q_tokens_per_tile == 32 and t.num_splits == 1 and ws == 0
+    assert st == pa.PA_OK and t.q_tokens_per_tile == 64 and t.num_splits == 1 and ws == 0
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -77,6 +77,9 @@ def test_select_tiles_decode_and_prefill(lib):
     ("out_dtype", 7, pa.PA_ERR_INVALID_ARG),
     ("causal", 2, pa.PA_ERR_INVALID_ARG),
     ("scale", float("nan"), pa.PA_ERR_INVALID_ARG),
+    ("scale", 0.0, pa.PA_ERR_INVALID_ARG),
+    ("scale", -0.5, pa.PA_ERR_INVALID_ARG),
+    ("scale", float("inf"), pa.PA_ERR_INVALID_ARG),
     ("num_kv_heads", 1, pa.PA_ERR_UNSUPPORTED),       # G = 32 not built
 ])
 def test_select_tiles_rejects(lib, field, value, status):
