@@ -38,6 +38,7 @@ constexpr int kKvTile = 32;          // keys per inner step
 constexpr int kLdsStride = kHeadDim + 8;  // K: bf16 elements per LDS row (272 B)
 constexpr int kVtStride = kKvTile + 4;    // V^T: bf16 elements per LDS row (72 B)
 constexpr int kBufs = 3;                  // LDS tile buffers
+constexpr int kPageCache = 2048;          // block-table entries staged in LDS (32k keys)
 constexpr float kLazyThreshold = 8.0f;
 
 // Find (sequence, query tile) of workgroup x: tiles are numbered sequence by
@@ -141,9 +142,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p, i
   const uint16_t* src = (v_side ? p.v_pool : p.k_pool) + (int64_t)g * p.stride_head;
   const int kp = tid & 15, dc = (tid & 255) >> 4;
   uint4 reg[2];
+  // The sequence's page ids, staged in LDS once, keep the block-table lookup
+  // off each tile's load path; blocks past the staged window read the table.
+  __shared__ int pg_lds[kPageCache];
+  {
+    // every key load_tile reads: below L and inside the nkv tiles
+    const int keys = min(L, nkv * kKvTile);
+    const int npg = min((keys + kPage - 1) / kPage, kPageCache);
+    for (int i = tid; i < npg; i += kThreads) pg_lds[i] = bt[i];
+    __syncthreads();
+  }
   auto load_tile = [&](int j) {
     const int key = j * kKvTile + 2 * kp;
-    const int64_t page = key < L ? bt[key / kPage] : 0;
+    const int blk = key / kPage;
+    const int64_t page = key < L ? (blk < kPageCache ? pg_lds[blk] : bt[blk]) : 0;
     const int64_t off = page * p.stride_page + (int64_t)(key % kPage) * p.stride_token + 8 * dc;
     const uint4 z = make_uint4(0, 0, 0, 0);
     reg[0] = key < L ? ld16(src + off) : z;
