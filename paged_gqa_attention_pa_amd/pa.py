@@ -166,6 +166,22 @@ def _check_tensors(q, k_pool, v_pool, block_tables, context_lens, out, lse):
         raise ValueError("lse must be contiguous fp32 [T, Hq] on q's device")
 
 
+def _check_problem(problem: Problem, q: torch.Tensor, out: torch.Tensor, k_pool: torch.Tensor,
+                   block_tables: torch.Tensor, num_seqs: int):
+    """A caller-built pa_problem must describe the tensors actually passed."""
+    odt = PA_FP32 if out.dtype == torch.float32 else PA_BF16
+    if problem.out_dtype != odt:
+        raise ValueError("problem.out_dtype does not match out.dtype")
+    T, Hq, D = q.shape
+    if (problem.total_query_tokens != T or problem.num_q_heads != Hq or problem.head_dim != D
+            or problem.num_seqs != num_seqs or problem.num_kv_heads != k_pool.shape[2]
+            or problem.page_size != k_pool.shape[1]
+            or problem.max_blocks_per_seq != block_tables.shape[1]
+            or (problem.kv_stride_page, problem.kv_stride_token, problem.kv_stride_head)
+            != tuple(int(x) for x in k_pool.stride()[:3])):
+        raise ValueError("problem does not match the tensors' shapes or strides")
+
+
 def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
            max_context_len: int, out: Optional[torch.Tensor] = None,
@@ -186,6 +202,8 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     if problem is None:
         problem = make_problem(q, k_pool, block_tables, B, scale, max_context_len, 1,
                                causal=True, out_dtype=out.dtype)
+    else:
+        _check_problem(problem, q, out, k_pool, block_tables, B)
     if tiles is None:
         tiles, ws = select_tiles(problem)
     else:
@@ -221,6 +239,8 @@ def prefill(q: torch.Tensor, query_start_loc: torch.Tensor, k_pool: torch.Tensor
     if problem is None:
         problem = make_problem(q, k_pool, block_tables, B, scale, max_context_len,
                                max_query_len, causal=causal, out_dtype=out.dtype)
+    else:
+        _check_problem(problem, q, out, k_pool, block_tables, B)
     if tiles is None:
         tiles, ws = select_tiles(problem)
     else:
