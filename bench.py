@@ -64,6 +64,9 @@ def parse():
                          "kernel for scaling HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--all", action="store_true",
+                    help="also time the other workloads (decode_ctx512, decode_b64, "
+                         "mixed_unified) and report them under 'others'")
     return ap.parse_args()
 
 
@@ -150,8 +153,17 @@ def bench_decode(torch, pa, workloads, args, dev):
                 pool_bytes=sum(p[0].numel() * 2 * 2 for p in pools))
 
 
-def bench_prefill(torch, pa, workloads, dev, steps, warmup):
-    spec = workloads.WORKLOADS["prefill_chunk2048"]
+def prefill_bytes(b):
+    """KV bytes the causal rows read (4096 per key) plus Q and O."""
+    kv = 0
+    for L, q in zip(b.context_lens.tolist(), b.query_lens):
+        kv += L * DECODE_BYTES_PER_TOKEN if q else 0
+    qo = 2 * b.q.numel() * 2
+    return kv + qo
+
+
+def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2048"):
+    spec = workloads.WORKLOADS[name]
     b = workloads.generate(spec, dev, fill="zero")
     max_ctx, max_q = b.max_context_len, b.max_query_len
     problem = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
@@ -172,11 +184,15 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup):
         step()
     total_ms, per = time_replays(torch, g, [g], steps, warmup)
     flops = prefill_flops(b)
+    nbytes = prefill_bytes(b)
     avg_ms = sum(per) / len(per)
     tfs = flops / (avg_ms * 1e-3) / 1e12
-    return {"workload": "prefill_chunk2048 (B=4, 1024 cached + 2048 new tokens, causal)",
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    whole = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (avg_ms * 1e-3)
+    return {"workload": name,
             "metric": "prefill attention TFLOP/s (causal pairs, 4*D flop each)",
             "value": round(tfs, 2), "unit": "TFLOP/s", "ms_per_step": round(avg_ms, 4),
+            "gb_per_s": round(gbs, 1), "whole_launch_roofline_frac": round(whole, 4),
             "tiles": tiles.as_dict(),
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
@@ -288,6 +304,24 @@ def main():
         result["prefill"] = bench_prefill(torch, pa, workloads, dev, max(5, args.steps // 5),
                                           min(args.warmup, 3))
         note(f"prefill: {result['prefill']['value']} TFLOP/s")
+    if args.all:
+        others = {}
+        for name in ("decode_ctx512", "decode_b64"):
+            sub = argparse.Namespace(**{**vars(args), "workload": name, "splits": 0, "waves": 0,
+                                        "variant": -1, "pools": 2 if name == "decode_b64" else 6})
+            dd = bench_decode(torch, pa, workloads, sub, dev)
+            ms = dd["total_ms"] / args.steps
+            others[name] = {"us_per_step": round(ms * 1e3, 2),
+                            "kv_gb_per_s": round(dd["nbytes"] / (ms * 1e-3) / 1e9, 1),
+                            "num_splits": dd["tiles"].num_splits}
+            note(f"{name}: {others[name]}")
+            del dd
+        mixed = bench_prefill(torch, pa, workloads, dev, max(5, args.steps // 5),
+                              min(args.warmup, 3), name="mixed_unified")
+        others["mixed_unified"] = mixed
+        note(f"mixed_unified: {mixed['ms_per_step'] * 1e3:.1f} us, {mixed['gb_per_s']} GB/s, "
+             f"{mixed['value']} TFLOP/s, whole-launch frac {mixed['whole_launch_roofline_frac']}")
+        result["others"] = others
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(workloads, b, args.cpu_seconds)
         note(f"cpu baseline: {result['cpu_baseline']}")

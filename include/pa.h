@@ -122,9 +122,11 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
  * each sequence is cut into S contiguous, page-aligned ranges processed by
  * different workgroups; their (normalised output, lse) partials go to the
  * workspace and are merged by log-sum-exp in the same call.
- * The merge runs inside the same launch: the last workgroup of a (sequence,
- * kv head) to finish, found with an atomic arrival counter, merges that
- * sequence's partials, so one decode call is one kernel.
+ * With tiles->variant bit 1 set (the table's choice) a second kernel, the
+ * one behind pa_splitkv_reduce, merges them; with it clear the merge runs
+ * inside the same launch: the last workgroup of a (sequence, kv head) to
+ * finish, found with an atomic arrival counter, merges that sequence's
+ * partials, so the call is one kernel.
  * q: bf16 [B, Hq, D]; out: [B, Hq, D] of problem->out_dtype; lse: fp32
  * [B, Hq] or NULL.  workspace: >= pa_workspace_size bytes, 256-byte aligned,
  * may be NULL when that size is 0.  It holds the partials and the arrival
@@ -142,9 +144,19 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
  * query rows [query_start_loc[s], query_start_loc[s+1]); those tokens are
  * the last q_len(s) positions of its context (already written to the pages),
  * so they attend to the cached prefix and, with causal set, causally to each
- * other.  Query length 1 rows (decode sequences) may be mixed in.
+ * other.  Query length 1 rows (decode sequences) may be mixed in, in any
+ * order, as one launch ([IBM-PA], unified kernel for mixed batches):
+ * sequences with more than one query token are cut into tiles of
+ * q_tokens_per_tile tokens x G heads, each walking its allowed keys; when
+ * the bounds admit single-token sequences (max_query_len <= 1, or
+ * total_query_tokens < num_seqs * max_query_len) and G <= 8, the same launch
+ * also holds split-KV decode workgroups for every (sequence, kv head,
+ * split), which return at once for sequences whose query length is not 1.
+ * Their partials are merged by a second kernel when tiles->num_splits > 1.
+ * With G = 16 single-token sequences take the tile path.
  * q: bf16 [T, Hq, D]; out: [T, Hq, D] of out_dtype; lse: fp32 [T, Hq] or NULL.
- * Workspace as for pa_decode. */
+ * workspace: >= pa_workspace_size bytes (partials for num_seqs * Hq rows),
+ * zero-filled before first use, as for pa_decode. */
 pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const void* q,
                      const int32_t* query_start_loc, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, const int32_t* context_lens, void* out,

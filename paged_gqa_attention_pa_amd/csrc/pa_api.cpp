@@ -69,6 +69,13 @@ DecodeWorkspace decode_workspace(int64_t rows, int splits, int head_dim, int64_t
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Can a prefill-type batch hold single-token (decode) sequences?  Host
+// bounds only: yes unless every sequence has exactly max_query_len tokens.
+bool may_hold_decode_rows(const pa_problem* pb) {
+  return pb->max_query_len <= 1 ||
+         (int64_t)pb->total_query_tokens < (int64_t)pb->num_seqs * pb->max_query_len;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,9 +97,8 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
   if (st != PA_OK) return st;
   if ((st = check_tiles(tiles)) != PA_OK) return st;
   if (!workspace_bytes) return PA_ERR_INVALID_ARG;
-  const int64_t rows = (int64_t)problem->max_query_len <= 1
-                           ? (int64_t)problem->num_seqs * problem->num_q_heads
-                           : (int64_t)problem->total_query_tokens * problem->num_q_heads;
+  // split partials are kept per (sequence, q head): decode rows only
+  const int64_t rows = (int64_t)problem->num_seqs * problem->num_q_heads;
   *workspace_bytes = decode_workspace(rows, tiles->num_splits, problem->head_dim,
                                       (int64_t)problem->num_seqs * problem->num_kv_heads)
                          .total;
@@ -119,9 +125,14 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     t.kv_tile = 32;
     t.waves_per_wg = 8;
     t.q_tokens_per_tile = 256 / G;
-    t.num_splits = 1;
+    // single-token sequences of a mixed batch run as split-KV decode work
+    t.num_splits = may_hold_decode_rows(problem)
+                       ? pa::table_decode_splits(problem->num_seqs, problem->num_kv_heads,
+                                                 problem->max_context_len)
+                       : 1;
     // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18
-    t.variant = problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0;
+    t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
+                pa::kVariantSeparateMerge;
   }
   *out = t;
   return pa_workspace_size(problem, &t, workspace_bytes);
@@ -163,6 +174,7 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   p.part_o = nullptr;
   p.part_lse = nullptr;
   p.counters = nullptr;
+  p.query_start_loc = nullptr;
   if (S > 1) {
     char* ws = static_cast<char*>(workspace);
     p.part_o = reinterpret_cast<float*>(ws + wl.o_off);
@@ -192,6 +204,8 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
     r.num_splits = S;
     r.head_dim = problem->head_dim;
     r.out_f32 = p.out_f32;
+    r.query_start_loc = nullptr;
+    r.num_q_heads = problem->num_q_heads;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -202,19 +216,29 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
                      const int32_t* block_tables, const int32_t* context_lens, void* out,
                      float* lse, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   pa_status st = check_problem(problem);
   if (st != PA_OK) return st;
   if ((st = check_tiles(tiles)) != PA_OK) return st;
-  if (tiles->num_splits != 1) return PA_ERR_UNSUPPORTED;
+  const int G = problem->num_q_heads / problem->num_kv_heads;
   if (!q || !query_start_loc || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PA_ERR_INVALID_ARG;
+  // G = 16 has no decode workgroups in this launch: its single-token
+  // sequences take the prefill tiles
+  const bool decode_rows = may_hold_decode_rows(problem) && G <= 8;
+  const int S = decode_rows ? tiles->num_splits : 1;
+  const int64_t rows = (int64_t)problem->num_seqs * problem->num_q_heads;
+  const DecodeWorkspace wl = decode_workspace(rows, S, problem->head_dim,
+                                              (int64_t)problem->num_seqs * problem->num_kv_heads);
+  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total ||
+                       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+    return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0 || problem->total_query_tokens == 0) return PA_OK;
-  const int G = problem->num_q_heads / problem->num_kv_heads;
   const int qt = 256 / G;
+  const float scale_log2 = problem->scale * pa::kLog2eHost;
+  const int out_f32 = problem->out_dtype == PA_FP32;
+
   pa::PrefillParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.query_start_loc = query_start_loc;
@@ -232,14 +256,65 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   p.num_kv_heads = problem->num_kv_heads;
   p.max_blocks = problem->max_blocks_per_seq;
   p.q_tile = qt;
+  p.decode_rows_apart = decode_rows ? 1 : 0;
   p.causal = problem->causal;
-  p.scale_log2 = problem->scale * pa::kLog2eHost;
-  p.out_f32 = problem->out_dtype == PA_FP32;
+  p.scale_log2 = scale_log2;
+  p.out_f32 = out_f32;
+
+  pa::DecodeParams d;
+  d.q = p.q;
+  d.k_pool = p.k_pool;
+  d.v_pool = p.v_pool;
+  d.block_tables = block_tables;
+  d.context_lens = context_lens;
+  d.out = out;
+  d.lse = lse;
+  d.part_o = nullptr;
+  d.part_lse = nullptr;
+  d.counters = nullptr;
+  d.query_start_loc = query_start_loc;
+  if (S > 1) {
+    char* ws = static_cast<char*>(workspace);
+    d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    d.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+    d.counters = reinterpret_cast<int32_t*>(ws + wl.ctr_off);
+  }
+  d.stride_page = p.stride_page;
+  d.stride_token = p.stride_token;
+  d.stride_head = p.stride_head;
+  d.num_seqs = problem->num_seqs;
+  d.num_q_heads = problem->num_q_heads;
+  d.num_kv_heads = problem->num_kv_heads;
+  d.max_blocks = problem->max_blocks_per_seq;
+  d.num_splits = S;
+  const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
+  d.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
+  d.scale_log2 = scale_log2;
+  d.out_f32 = out_f32;
+
   // static grid: sum over sequences of ceil(q_len / qt) <= ceil(T / qt) + B
-  const int64_t grid_x = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
-  if (grid_x > 0x7fffffff) return PA_ERR_UNSUPPORTED;
-  return from_hip(pa::launch_prefill(p, G, (int)grid_x,
-                                    (tiles->variant & pa::kVariantPreciseP) != 0, stream));
+  const int64_t nx = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
+  const int64_t n_dec =
+      decode_rows ? (int64_t)problem->num_seqs * problem->num_kv_heads * S : 0;
+  if (nx * problem->num_kv_heads + n_dec > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
+  if ((st = from_hip(pa::launch_prefill(p, d, G, (int)nx, (int)n_dec, precise, stream))) != PA_OK)
+    return st;
+  if (decode_rows && S > 1) {
+    pa::ReduceParams r;
+    r.part_o = d.part_o;
+    r.part_lse = d.part_lse;
+    r.out = out;
+    r.lse = lse;
+    r.rows = (int32_t)rows;
+    r.num_splits = S;
+    r.head_dim = problem->head_dim;
+    r.out_f32 = out_f32;
+    r.query_start_loc = query_start_loc;
+    r.num_q_heads = problem->num_q_heads;
+    st = from_hip(pa::launch_reduce(r, stream));
+  }
+  return st;
 }
 
 pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, int32_t rows,
@@ -261,6 +336,8 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
   r.num_splits = num_splits;
   r.head_dim = head_dim;
   r.out_f32 = out_dtype == PA_FP32;
+  r.query_start_loc = nullptr;
+  r.num_q_heads = 1;
   return from_hip(pa::launch_reduce(r, stream));
 }
 

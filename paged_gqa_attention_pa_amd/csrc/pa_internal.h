@@ -28,6 +28,7 @@ struct DecodeParams {
   float* part_o;            // [B*Hq, S, D] when S > 1
   float* part_lse;          // [B*Hq, S]
   int32_t* counters;        // [B*Hkv] split arrival counters, zero between calls
+  const int32_t* query_start_loc;  // mixed batch: [B+1]; null for a pure decode batch
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
   int32_t tiles_per_split;  // 16-key tiles per split
@@ -48,6 +49,7 @@ struct PrefillParams {
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
   int32_t q_tile;           // query tokens per workgroup
+  int32_t decode_rows_apart;  // 1: single-token sequences run as decode workgroups
   int32_t causal;
   float scale_log2;
   int32_t out_f32;
@@ -59,13 +61,19 @@ struct ReduceParams {
   void* out;                // [rows, D]
   float* lse;               // [rows] or null
   int32_t rows, num_splits, head_dim, out_f32;
+  // Mixed batch: rows are (sequence, q head) pairs, only single-token
+  // sequences are merged, into output row query_start_loc[s]*Hq + h.
+  const int32_t* query_start_loc;  // null: output row = partial row
+  int32_t num_q_heads;
 };
 
 // Launchers: return hipSuccess or the launch error.  Shapes were checked.
 hipError_t launch_decode(const DecodeParams& p, int group, int waves, bool fused,
                          hipStream_t stream);
-hipError_t launch_prefill(const PrefillParams& p, int group, int grid_x, bool precise_p,
-                          hipStream_t stream);
+// Prefill tiles (nx x Hkv workgroups) and n_dec decode workgroups (split x
+// Hkv x B, for the single-token sequences of a mixed batch) in one launch.
+hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
+                          int n_dec, bool precise_p, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 
 }  // namespace pa

@@ -1,0 +1,326 @@
+// Paged GQA prefill body (bf16 MFMA) for gfx950.
+//
+// One workgroup = (query tile of one sequence, kv head).  Its Q-block is
+// 256 rows: QT = 256 / G query tokens x the G query heads that share the KV
+// head (the Q-Block step of the IBM Triton summary's five-step list), row
+// r -> token r / G, head r % G; wavefront w owns rows 32w..32w+31 and each
+// lane owns one row (lane % 32).  The workgroup walks the sequence's keys in
+// tiles of 32 (two pages), up to the causal limit of its last token, staging
+// each K and V tile in LDS once for all eight wavefronts (FlashAttention-style
+// tiling, guide sections "Flash Attention革命" and "Triton实现Flash
+// Attention"):
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, K rows from LDS (16-byte reads),
+//                 Q^T held in registers; lane l receives 16 keys of row l%32.
+//   online softmax in the log2 domain with a lazily raised running max;
+//   masked keys (past the context, or after the row's causal position) are
+//   removed by select.
+//   O^T += V^T P^T  v_mfma_f32_32x32x16_bf16; P (rounded to bf16) is already
+//                 in the B-operand layout the S^T result left it in; V^T is
+//                 gathered from LDS.  The precise variant splits P into a bf16
+//                 high part and a bf16 remainder (two MFMAs), leaving a
+//                 relative weight error of about 2^-18 instead of 2^-9.
+// Each sequence's query tokens are the last q_len positions of its context:
+// query token i sees keys j <= L - q_len + i (bottom-right causal alignment,
+// so a chunk attends to its cached prefix in full).  The grid is static:
+// x runs over a host bound on query tiles; each workgroup finds its
+// sequence by a scan of query_start_loc and surplus workgroups exit.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace prefill_detail {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;   // Q-block rows per workgroup
+constexpr int kKvTile = 32;          // keys per inner step
+constexpr int kLdsStride = kHeadDim + 8;  // K: bf16 elements per LDS row (272 B)
+constexpr int kVtStride = kKvTile + 4;    // V^T: bf16 elements per LDS row (72 B)
+constexpr int kBufs = 3;                  // LDS tile buffers
+constexpr int kPageCache = 2048;          // block-table entries staged in LDS (32k keys)
+constexpr float kLazyThreshold = 8.0f;
+
+// Find (sequence, query tile) of workgroup x: tiles are numbered sequence by
+// sequence, ceil(q_len / qt) per sequence (none for single-token sequences
+// when skip_single: those run as decode workgroups).  Returns false for a
+// surplus x.
+__device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool skip_single,
+                          int* seq, int* tile) {
+  __shared__ int s_found[2];
+  __shared__ int s_wsum[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_found[0] = -1;
+  int base = 0;
+  for (int c0 = 0; c0 < num_seqs; c0 += 64 * kWaves) {
+    const int s = c0 + tid;
+    int cnt = 0;
+    if (s < num_seqs) {
+      const int ql = qsl[s + 1] - qsl[s];
+      cnt = (skip_single && ql == 1) ? 0 : (ql + qt - 1) / qt;
+    }
+    int v = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    __syncthreads();
+    if (lane == 63) s_wsum[wave] = v;
+    __syncthreads();
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) wbase += s_wsum[w];
+      total += s_wsum[w];
+    }
+    const int incl = base + wbase + v;
+    if (cnt > 0 && x >= incl - cnt && x < incl) {
+      s_found[0] = s;
+      s_found[1] = x - (incl - cnt);
+    }
+    base += total;
+    __syncthreads();
+    if (s_found[0] >= 0 || x < base) break;
+  }
+  *seq = s_found[0];
+  *tile = s_found[1];
+  return s_found[0] >= 0;
+}
+
+// LDS bytes prefill_body needs from its caller (K tiles, V^T tiles, page ids).
+constexpr int kPrefillSmemBytes =
+    kBufs * kKvTile * kLdsStride * 2 + kBufs * kHeadDim * kVtStride * 2 + kPageCache * 4;
+
+// One workgroup of kThreads threads: query tile / KV head number `id` of the
+// 1-D prefill grid (nx tiles x Hkv).  smem: kPrefillSmemBytes, 16-byte aligned.
+template <int G, bool PRECISE>
+__device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int nx,
+                                             char* smem) {
+  constexpr int D = kHeadDim;
+  constexpr int QT = kRows / G;
+  // 1-D grid: id -> (kv head, query tile).  Consecutive ids go to different
+  // XCDs, so with Hkv = 8 each XCD serves one KV head and its K/V stay in
+  // that XCD's L2.  Query tiles run from the last (heaviest under the causal
+  // mask) to the first.
+  const int g = id % p.num_kv_heads;
+  const int x = nx - 1 - id / p.num_kv_heads;
+  int s, qtile;
+  if (!find_tile(p.query_start_loc, p.num_seqs, QT, x, p.decode_rows_apart != 0, &s, &qtile))
+    return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int q0 = p.query_start_loc[s];
+  const int qlen = p.query_start_loc[s + 1] - q0;
+  const int L = p.context_lens[s];
+  const int tok0 = qtile * QT;
+  const int ntok = min(QT, qlen - tok0);
+
+  // This lane's row: token r / G, head r % G.
+  const int r = 32 * wave + n;
+  const int tl = r / G, h = r % G;
+  const bool row_valid = tl < ntok;
+  const int qi = tok0 + tl;  // index of the token inside the chunk
+  const int key_limit = p.causal ? min(L, L - qlen + qi + 1) : L;  // keys < limit
+  // smallest limit among this wave's rows (its first token): tiles that end
+  // below it need no mask
+  const int wave_limit = p.causal ? min(L, L - qlen + tok0 + (32 * wave) / G + 1) : L;
+  const int kv_end = p.causal ? min(L, L - qlen + tok0 + ntok) : L;
+  const int nkv = kv_end > 0 ? (kv_end + kKvTile - 1) / kKvTile : 0;
+
+  // Q^T operand: lane holds Q[row][16ks + 8*half .. +8] for ks = 0..7.
+  bf16x8 qb[8];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)(q0 + qi) * p.num_q_heads + g * G + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      qb[ks] = row_valid ? as_bf16x8(ld16(qrow + 16 * ks)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+
+  // LDS, three buffers: K row-major [key][dim] (272-byte rows), V transposed
+  // [dim][key] (72-byte rows: 32 keys + pad), so both MFMA operands are plain
+  // 16- and 8-byte LDS reads.  While tile j is being finished (softmax, P.V),
+  // the S^T MFMAs of tile j+1 already run and tile j+2 is being stored: one
+  // barrier per tile.
+  auto k_lds = reinterpret_cast<uint16_t(*)[kKvTile * kLdsStride]>(smem);
+  auto vt_lds = reinterpret_cast<uint16_t(*)[D * kVtStride]>(smem + kBufs * kKvTile * kLdsStride * 2);
+
+  // Tile loader: threads 0..255 stage K, threads 256..511 stage V; thread t
+  // (mod 256) handles keys 2*(t%16), 2*(t%16)+1 (same page) and dims
+  // 8*((t%256)/16) .. +7.
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
+  const bool v_side = tid >= 256;
+  const uint16_t* src = (v_side ? p.v_pool : p.k_pool) + (int64_t)g * p.stride_head;
+  const int kp = tid & 15, dc = (tid & 255) >> 4;
+  uint4 reg[2];
+  // The sequence's page ids, staged in LDS once, keep the block-table lookup
+  // off each tile's load path; blocks past the staged window read the table.
+  int* pg_lds = reinterpret_cast<int*>(smem + kBufs * kKvTile * kLdsStride * 2 +
+                                       kBufs * D * kVtStride * 2);
+  {
+    // every key load_tile reads: below L and inside the nkv tiles
+    const int keys = min(L, nkv * kKvTile);
+    const int npg = min((keys + kPage - 1) / kPage, kPageCache);
+    for (int i = tid; i < npg; i += kThreads) pg_lds[i] = bt[i];
+    __syncthreads();
+  }
+  auto load_tile = [&](int j) {
+    const int key = j * kKvTile + 2 * kp;
+    const int blk = key / kPage;
+    const int64_t page = key < L ? (blk < kPageCache ? pg_lds[blk] : bt[blk]) : 0;
+    const int64_t off = page * p.stride_page + (int64_t)(key % kPage) * p.stride_token + 8 * dc;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    reg[0] = key < L ? ld16(src + off) : z;
+    reg[1] = key + 1 < L ? ld16(src + off + p.stride_token) : z;
+  };
+  auto store_tile = [&](int buf) {
+    if (!v_side) {
+      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp) * kLdsStride + 8 * dc]) = reg[0];
+      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp + 1) * kLdsStride + 8 * dc]) = reg[1];
+    } else {
+      const uint32_t a[4] = {reg[0].x, reg[0].y, reg[0].z, reg[0].w};
+      const uint32_t b[4] = {reg[1].x, reg[1].y, reg[1].z, reg[1].w};
+      uint32_t* vt = reinterpret_cast<uint32_t*>(&vt_lds[buf][0]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // dims 8dc+2w and 8dc+2w+1: (key 2kp, key 2kp+1) pairs
+        vt[((8 * dc + 2 * w) * kVtStride + 2 * kp) / 2] = (a[w] & 0xffffu) | (b[w] << 16);
+        vt[((8 * dc + 2 * w + 1) * kVtStride + 2 * kp) / 2] = (a[w] >> 16) | (b[w] & 0xffff0000u);
+      }
+    }
+  };
+  // S^T = K Q^T for the tile in buffer buf, D = 128 in 8 steps of 16.
+  auto qk = [&](int buf, f32x16& st) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      // two 8-byte LDS reads: measured faster than one 16-byte read on gfx950
+      const uint16_t* kr = &k_lds[buf][n * kLdsStride + 16 * ks + 8 * half];
+      const uint2 a0 = *reinterpret_cast<const uint2*>(kr);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(kr + 4);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)), qb[ks], st, 0, 0, 0);
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[mt][e] = 0.f;
+  float m = kNegInf, lsum = 0.f;
+  const float c = p.scale_log2;  // > 0 (checked on the host)
+
+#pragma unroll
+  for (int j = 0; j < kBufs - 1; ++j)
+    if (j < nkv) {
+      load_tile(j);
+      store_tile(j);
+    }
+  __syncthreads();
+  if (kBufs - 1 < nkv) load_tile(kBufs - 1);
+  f32x16 st_cur, st_next;
+  if (nkv > 0) qk(0, st_cur);
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j % kBufs;
+    if (j + 1 < nkv) qk((j + 1) % kBufs, st_next);  // MFMA pipe, overlaps the softmax below
+
+    // Register e holds key 8*(e/4) + 4*half + e%4 of tile j, row n; the
+    // log2-domain logit is c*S (c > 0, so the max can be taken on S).
+    float smax = kNegInf;
+    const bool full = j * kKvTile + kKvTile <= wave_limit;  // no key of the tile masked
+    if (!full) {
+      const int kbase = j * kKvTile + 4 * half;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + (e & 3);
+        st_cur[e] = (key < key_limit) ? st_cur[e] : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, st_cur[e]);
+    const float tmax = fmaxf(smax, shfl_xor(smax, 32)) * c;
+    const bool need = tmax > m + kLazyThreshold;
+    if (wave_any(need)) {
+      const float m_new = need ? tmax : m;
+      const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[mt][e] *= alpha;
+    }
+    const float neg_m = (m == kNegInf) ? 0.f : -m;
+    uint32_t pk[8], pl[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = fast_exp2(fmaf(st_cur[e], c, neg_m));
+      const float p1 = fast_exp2(fmaf(st_cur[e + 1], c, neg_m));
+      psum += p0 + p1;
+      pk[e >> 1] = pack_bf16x2(p0, p1);
+      if constexpr (PRECISE) {
+        pl[e >> 1] = pack_bf16x2(p0 - bf16lo(pk[e >> 1]), p1 - bf16hi(pk[e >> 1]));
+      }
+    }
+    lsum += psum;
+
+    // O^T += V^T P^T: two k-steps of 16 keys, four 32-dim M tiles.
+    const uint16_t* vt = &vt_lds[buf][0];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * kk], pk[4 * kk + 1],
+                                                              pk[4 * kk + 2], pk[4 * kk + 3]));
+      bf16x8 pbl;
+      if constexpr (PRECISE)
+        pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2],
+                                                    pl[4 * kk + 3]));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint16_t* row = vt + (32 * mt + n) * kVtStride + 16 * kk + 4 * half;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row);      // keys +0..3
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 8);  // keys +8..11
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[mt], 0, 0, 0);
+        if constexpr (PRECISE)
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbl, o[mt], 0, 0, 0);
+      }
+    }
+    // Tile j+2 goes to the buffer tile j-1 used (its last reads were before
+    // the previous barrier); its global loads were issued an iteration ago.
+    if (j + kBufs - 1 < nkv) store_tile((j + kBufs - 1) % kBufs);
+    __syncthreads();
+    if (j + kBufs < nkv) load_tile(j + kBufs);
+    st_cur = st_next;
+  }
+
+  const float l = lsum + shfl_xor(lsum, 32);
+  if (!row_valid) return;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  const int64_t orow = (int64_t)(q0 + qi) * p.num_q_heads + g * G + h;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int d = 32 * mt + 8 * rb + 4 * half;
+      const float a0 = o[mt][4 * rb] * inv, a1 = o[mt][4 * rb + 1] * inv;
+      const float a2 = o[mt][4 * rb + 2] * inv, a3 = o[mt][4 * rb + 3] * inv;
+      if (p.out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + orow * D + d) =
+            make_float4(a0, a1, a2, a3);
+      } else {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + orow * D + d) =
+            make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+      }
+    }
+  if (p.lse && half == 0) p.lse[orow] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
+}
+
+}  // namespace prefill_detail
+}  // namespace pa

@@ -42,6 +42,13 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
   __shared__ float scratch[kThreads / 64];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  int64_t orow = row;
+  if (p.query_start_loc) {  // mixed batch: merge the single-token sequences only
+    const int s = row / p.num_q_heads;
+    const int q0 = p.query_start_loc[s];
+    if (p.query_start_loc[s + 1] - q0 != 1) return;
+    orow = (int64_t)q0 * p.num_q_heads + row % p.num_q_heads;
+  }
   const int S = p.num_splits;
   const int D = p.head_dim;
   const float* lse_row = p.part_lse + (int64_t)row * S;
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
       }
       acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-      const int64_t off = (int64_t)row * D + 4 * (base + tid);
+      const int64_t off = orow * D + 4 * (base + tid);
       if (p.out_f32) {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) = acc;
       } else {
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
       }
     }
   }
-  if (p.lse && tid == 0) p.lse[row] = (M == kNegInf) ? kNegInf : M + fast_log2(wsum) * kLn2;
+  if (p.lse && tid == 0) p.lse[orow] = (M == kNegInf) ? kNegInf : M + fast_log2(wsum) * kLn2;
 }
 
 }  // namespace
