@@ -95,7 +95,7 @@ typedef struct pa_problem {
 /* Launch shape chosen by pa_select_tiles (or forced by a tuning sweep). */
 typedef struct pa_tiles {
   int32_t kv_tile;           /* keys per inner step (16 decode; 32/64 prefill)   */
-  int32_t num_splits;        /* split-KV count S (>= 1)                          */
+  int32_t num_splits;        /* split-KV count S of decode rows (>= 1)           */
   int32_t waves_per_wg;      /* wavefronts per workgroup                         */
   int32_t q_tokens_per_tile; /* query tokens per prefill workgroup               */
   int32_t variant;           /* bit 0 (prefill): carry P as a bf16 high part plus a  */
@@ -104,6 +104,14 @@ typedef struct pa_tiles {
                              /* bit 1 (decode, S > 1): merge the splits in a second  */
                              /* kernel (pa_splitkv_reduce's) instead of in the last  */
                              /* workgroup of each sequence                           */
+                             /* bit 2 (decode, S > 1, needs bit 1): even-work grid: */
+                             /* a fixed number of workgroups share all tiles of all */
+                             /* sequences equally (cut at any tile, merged by lse);  */
+                             /* a sequence is cut into at most S + 1 pieces          */
+  int32_t tile_splits;       /* pa_prefill: each query tile's keys are cut into     */
+                             /* this many runs of whole 32-key tiles (0 or 1: one   */
+                             /* run, at most 8), merged by log-sum-exp; it spreads  */
+                             /* a few long-prefix chunks over the whole chip         */
 } pa_tiles;
 
 /* Pick the launch shape for a problem from the built-in table (the offline
@@ -155,8 +163,12 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
  * Their partials are merged by a second kernel when tiles->num_splits > 1.
  * With G = 16 single-token sequences take the tile path.
  * q: bf16 [T, Hq, D]; out: [T, Hq, D] of out_dtype; lse: fp32 [T, Hq] or NULL.
- * workspace: >= pa_workspace_size bytes (partials for num_seqs * Hq rows),
- * zero-filled before first use, as for pa_decode. */
+ * With tiles->tile_splits > 1 every query tile's keys are split as well and
+ * its partials ([T * Hq, tile_splits, D] fp32 plus lse) are merged by a
+ * further kernel.
+ * workspace: >= pa_workspace_size bytes (decode-row partials for
+ * num_seqs * Hq rows, tile partials for T * Hq rows), zero-filled before
+ * first use, as for pa_decode. */
 pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const void* q,
                      const int32_t* query_start_loc, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, const int32_t* context_lens, void* out,

@@ -46,24 +46,52 @@ pa_status check_problem(const pa_problem* pb) {
 pa_status check_tiles(const pa_tiles* t) {
   if (!t) return PA_ERR_INVALID_ARG;
   if (t->num_splits < 1 || t->num_splits > pa::kMaxSplits) return PA_ERR_INVALID_ARG;
+  if (t->tile_splits < 0 || t->tile_splits > pa::kMaxTileSplits) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
-// Decode workspace: partial O [rows, S, D] fp32, partial lse [rows, S] fp32,
-// and one int32 arrival counter per (sequence, kv head); 256-byte aligned
-// regions.  The counters must be zero before the first call; every call
-// leaves them zero.
-struct DecodeWorkspace {
-  size_t o_off, lse_off, ctr_off, total;
+int tile_splits_of(const pa_problem* pb, const pa_tiles* t) {
+  return (pb->max_query_len > 1 && t->tile_splits > 1) ? t->tile_splits : 1;
+}
+
+// Workspace, 256-byte aligned regions:
+//  decode rows (num_splits > 1): partial O [B*Hq, slots, D] fp32, partial
+//    lse [B*Hq, slots] fp32 (slots = S, or S + 1 for the even-work grid), one
+//    int32 arrival counter per (sequence, kv head) and one int32 piece count
+//    per (sequence, kv head); the arrival counters must be zero before the
+//    first call, every call leaves them zero;
+//  query tiles (prefill problems, tile_splits > 1): partial O
+//    [T*Hq, tile_splits, D] fp32 and partial lse [T*Hq, tile_splits].
+// dec_total is the end of the decode-row part (all pa_decode needs).
+struct Workspace {
+  size_t o_off, lse_off, ctr_off, cnt_off, dec_total, to_off, tlse_off, total;
 };
 
-DecodeWorkspace decode_workspace(int64_t rows, int splits, int head_dim, int64_t counters) {
-  DecodeWorkspace w{0, 0, 0, 0};
-  if (splits <= 1) return w;
-  w.o_off = 0;
-  w.lse_off = align_up((size_t)rows * splits * head_dim * sizeof(float));
-  w.ctr_off = w.lse_off + align_up((size_t)rows * splits * sizeof(float));
-  w.total = w.ctr_off + align_up((size_t)counters * sizeof(int32_t));
+bool even_grid(const pa_tiles* t) {
+  return t->num_splits > 1 && (t->variant & pa::kVariantEvenWork) != 0;
+}
+
+Workspace workspace_layout(const pa_problem* pb, const pa_tiles* t) {
+  Workspace w{0, 0, 0, 0, 0, 0, 0, 0};
+  const int64_t D = pb->head_dim;
+  const int S = t->num_splits;
+  if (S > 1) {
+    const int64_t rows = (int64_t)pb->num_seqs * pb->num_q_heads;
+    const int64_t slots = S + (even_grid(t) ? 1 : 0);
+    const size_t units = (size_t)((int64_t)pb->num_seqs * pb->num_kv_heads);
+    w.lse_off = align_up((size_t)(rows * slots * D) * sizeof(float));
+    w.ctr_off = w.lse_off + align_up((size_t)(rows * slots) * sizeof(float));
+    w.cnt_off = w.ctr_off + align_up(units * sizeof(int32_t));
+    w.dec_total = w.cnt_off + align_up(units * sizeof(int32_t));
+  }
+  const int ts = tile_splits_of(pb, t);
+  w.total = w.dec_total;
+  if (ts > 1) {
+    const int64_t rows = (int64_t)pb->total_query_tokens * pb->num_q_heads;
+    w.to_off = w.dec_total;
+    w.tlse_off = w.to_off + align_up((size_t)(rows * ts * D) * sizeof(float));
+    w.total = w.tlse_off + align_up((size_t)(rows * ts) * sizeof(float));
+  }
   return w;
 }
 
@@ -97,11 +125,7 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
   if (st != PA_OK) return st;
   if ((st = check_tiles(tiles)) != PA_OK) return st;
   if (!workspace_bytes) return PA_ERR_INVALID_ARG;
-  // split partials are kept per (sequence, q head): decode rows only
-  const int64_t rows = (int64_t)problem->num_seqs * problem->num_q_heads;
-  *workspace_bytes = decode_workspace(rows, tiles->num_splits, problem->head_dim,
-                                      (int64_t)problem->num_seqs * problem->num_kv_heads)
-                         .total;
+  *workspace_bytes = workspace_layout(problem, tiles).total;
   return PA_OK;
 }
 
@@ -133,6 +157,17 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18
     t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
                 pa::kVariantSeparateMerge;
+    // Split query tiles only in batches without single-token sequences:
+    // measured on gfx950, decode workgroups already use the CUs that a few
+    // long query tiles leave idle, and splitting the tiles then only adds
+    // partial traffic (mixed 16 decodes + 2x512-token chunks: 255 us whole,
+    // 295 us with two runs per tile; the chunks alone: 197 us -> 134 us).
+    t.tile_splits = may_hold_decode_rows(problem)
+                        ? 1
+                        : pa::table_prefill_tile_splits(problem->total_query_tokens,
+                                                        t.q_tokens_per_tile,
+                                                        problem->num_kv_heads,
+                                                        problem->max_context_len);
   }
   *out = t;
   return pa_workspace_size(problem, &t, workspace_bytes);
@@ -154,11 +189,12 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   const int waves = tiles->waves_per_wg;
   if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
   if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
-  const int64_t rows = (int64_t)problem->num_seqs * problem->num_q_heads;
-  const DecodeWorkspace wl = decode_workspace(rows, S, problem->head_dim,
-                                              (int64_t)problem->num_seqs * problem->num_kv_heads);
-  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total ||
-                       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+  const bool even = even_grid(tiles);
+  // the even-work grid merges in the separate kernel only
+  if (even && (tiles->variant & pa::kVariantSeparateMerge) == 0) return PA_ERR_INVALID_ARG;
+  const Workspace wl = workspace_layout(problem, tiles);
+  if (wl.dec_total > 0 && (!workspace || workspace_bytes < wl.dec_total ||
+                           (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0) return PA_OK;
 
@@ -174,12 +210,14 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   p.part_o = nullptr;
   p.part_lse = nullptr;
   p.counters = nullptr;
+  p.piece_counts = nullptr;
   p.query_start_loc = nullptr;
   if (S > 1) {
     char* ws = static_cast<char*>(workspace);
     p.part_o = reinterpret_cast<float*>(ws + wl.o_off);
     p.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
     p.counters = reinterpret_cast<int32_t*>(ws + wl.ctr_off);
+    p.piece_counts = reinterpret_cast<int32_t*>(ws + wl.cnt_off);
   }
   p.stride_page = problem->kv_stride_page;
   p.stride_token = problem->kv_stride_token;
@@ -188,24 +226,35 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   p.num_q_heads = problem->num_q_heads;
   p.num_kv_heads = problem->num_kv_heads;
   p.max_blocks = problem->max_blocks_per_seq;
-  p.num_splits = S;
+  p.num_splits = even ? S + 1 : S;
   p.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
+  p.max_tiles = ntiles;
+  p.even_min_tiles = p.tiles_per_split;
   p.scale_log2 = problem->scale * pa::kLog2eHost;
   p.out_f32 = problem->out_dtype == PA_FP32;
   const bool separate = S > 1 && (tiles->variant & pa::kVariantSeparateMerge) != 0;
-  if ((st = from_hip(pa::launch_decode(p, G, waves, !separate, stream))) != PA_OK) return st;
+  if (even) {
+    const int nw = pa::decode_even_resident(G, waves);
+    if (nw <= 0) return PA_ERR_HIP;
+    if ((st = from_hip(pa::launch_decode_even(p, G, waves, nw, stream))) != PA_OK) return st;
+  } else if ((st = from_hip(pa::launch_decode(p, G, waves, !separate, stream))) != PA_OK) {
+    return st;
+  }
   if (separate) {
     pa::ReduceParams r;
     r.part_o = p.part_o;
     r.part_lse = p.part_lse;
     r.out = out;
     r.lse = lse;
-    r.rows = (int32_t)rows;
-    r.num_splits = S;
+    r.rows = problem->num_seqs * problem->num_q_heads;
+    r.num_splits = p.num_splits;
     r.head_dim = problem->head_dim;
     r.out_f32 = p.out_f32;
     r.query_start_loc = nullptr;
     r.num_q_heads = problem->num_q_heads;
+    r.piece_counts = even ? p.piece_counts : nullptr;
+    r.context_lens = context_lens;
+    r.group = G;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -228,9 +277,8 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   // sequences take the prefill tiles
   const bool decode_rows = may_hold_decode_rows(problem) && G <= 8;
   const int S = decode_rows ? tiles->num_splits : 1;
-  const int64_t rows = (int64_t)problem->num_seqs * problem->num_q_heads;
-  const DecodeWorkspace wl = decode_workspace(rows, S, problem->head_dim,
-                                              (int64_t)problem->num_seqs * problem->num_kv_heads);
+  const int TS = tile_splits_of(problem, tiles);
+  const Workspace wl = workspace_layout(problem, tiles);
   if (wl.total > 0 && (!workspace || workspace_bytes < wl.total ||
                        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
@@ -257,6 +305,14 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   p.max_blocks = problem->max_blocks_per_seq;
   p.q_tile = qt;
   p.decode_rows_apart = decode_rows ? 1 : 0;
+  p.tile_splits = TS;
+  p.tpart_o = nullptr;
+  p.tpart_lse = nullptr;
+  if (TS > 1) {
+    char* ws = static_cast<char*>(workspace);
+    p.tpart_o = reinterpret_cast<float*>(ws + wl.to_off);
+    p.tpart_lse = reinterpret_cast<float*>(ws + wl.tlse_off);
+  }
   p.causal = problem->causal;
   p.scale_log2 = scale_log2;
   p.out_f32 = out_f32;
@@ -289,6 +345,9 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.num_splits = S;
   const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
   d.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
+  d.max_tiles = ntiles;
+  d.even_min_tiles = 0;
+  d.piece_counts = nullptr;
   d.scale_log2 = scale_log2;
   d.out_f32 = out_f32;
 
@@ -296,22 +355,41 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   const int64_t nx = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
   const int64_t n_dec =
       decode_rows ? (int64_t)problem->num_seqs * problem->num_kv_heads * S : 0;
-  if (nx * problem->num_kv_heads + n_dec > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  if (nx * problem->num_kv_heads * TS + n_dec > 0x7fffffff) return PA_ERR_UNSUPPORTED;
   const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
   if ((st = from_hip(pa::launch_prefill(p, d, G, (int)nx, (int)n_dec, precise, stream))) != PA_OK)
     return st;
+  if (TS > 1) {
+    pa::TileMergeParams m;
+    m.tpart_o = p.tpart_o;
+    m.tpart_lse = p.tpart_lse;
+    m.query_start_loc = query_start_loc;
+    m.out = out;
+    m.lse = lse;
+    m.num_seqs = problem->num_seqs;
+    m.num_q_heads = problem->num_q_heads;
+    m.num_kv_heads = problem->num_kv_heads;
+    m.q_tile = qt;
+    m.decode_rows_apart = p.decode_rows_apart;
+    m.tile_splits = TS;
+    m.out_f32 = out_f32;
+    if ((st = from_hip(pa::launch_tile_merge(m, (int)nx, stream))) != PA_OK) return st;
+  }
   if (decode_rows && S > 1) {
     pa::ReduceParams r;
     r.part_o = d.part_o;
     r.part_lse = d.part_lse;
     r.out = out;
     r.lse = lse;
-    r.rows = (int32_t)rows;
+    r.rows = problem->num_seqs * problem->num_q_heads;
     r.num_splits = S;
     r.head_dim = problem->head_dim;
     r.out_f32 = out_f32;
     r.query_start_loc = query_start_loc;
     r.num_q_heads = problem->num_q_heads;
+    r.piece_counts = nullptr;
+    r.context_lens = context_lens;
+    r.group = G;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -338,6 +416,9 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
   r.out_f32 = out_dtype == PA_FP32;
   r.query_start_loc = nullptr;
   r.num_q_heads = 1;
+  r.piece_counts = nullptr;
+  r.context_lens = nullptr;
+  r.group = 1;
   return from_hip(pa::launch_reduce(r, stream));
 }
 

@@ -11,11 +11,13 @@ constexpr int kPage = 16;       // built page size
 constexpr int kDecodeTile = 16; // keys per decode step (one MFMA N-tile)
 constexpr int kMaxSplits = 256;        // decode split-KV
 constexpr int kReduceMaxSplits = 4096; // pa_splitkv_reduce
+constexpr int kMaxTileSplits = 8;      // prefill: splits of one query tile's keys
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 // pa_tiles.variant bits
 constexpr int kVariantPreciseP = 1;      // prefill: P as bf16 high + remainder
 constexpr int kVariantSeparateMerge = 2; // decode: merge splits in a second kernel
+constexpr int kVariantEvenWork = 4;      // decode: even-work grid (with the separate merge)
 
 struct DecodeParams {
   const uint16_t* q;        // [B, Hq, D] bf16
@@ -32,7 +34,10 @@ struct DecodeParams {
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
   int32_t tiles_per_split;  // 16-key tiles per split
-  int32_t num_splits;
+  int32_t num_splits;       // partial slots per row (even-work grid: splits + 1)
+  int32_t max_tiles;        // ceil(max_context_len / 16): bound on a unit's tiles
+  int32_t even_min_tiles;   // even-work grid: least tiles per workgroup
+  int32_t* piece_counts;    // even-work grid: [B*Hkv] pieces per unit
   float scale_log2;         // scale * log2(e)
   int32_t out_f32;
 };
@@ -50,6 +55,13 @@ struct PrefillParams {
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
   int32_t q_tile;           // query tokens per workgroup
   int32_t decode_rows_apart;  // 1: single-token sequences run as decode workgroups
+  // tile_splits > 1: each query tile's key range is cut into that many runs
+  // of whole 32-key tiles, one workgroup each, writing normalised partials
+  // (fp32, [T*Hq, tile_splits, D]) and their lse ([T*Hq, tile_splits],
+  // natural log) instead of out / lse; tile_merge_kernel combines them.
+  int32_t tile_splits;
+  float* tpart_o;
+  float* tpart_lse;
   int32_t causal;
   float scale_log2;
   int32_t out_f32;
@@ -65,15 +77,39 @@ struct ReduceParams {
   // sequences are merged, into output row query_start_loc[s]*Hq + h.
   const int32_t* query_start_loc;  // null: output row = partial row
   int32_t num_q_heads;
+  // Even-work decode grid: row (b, h) has piece_counts[b*Hkv + h/G] slots
+  // in use (rows of one piece were written directly and are skipped; rows of
+  // an empty context get O = 0, lse = -inf).  Null: every slot is in use.
+  const int32_t* piece_counts;
+  const int32_t* context_lens;
+  int32_t group;
+};
+
+// Merge of split query tiles: one workgroup per (query tile, kv head) of the
+// prefill grid, without the split index.
+struct TileMergeParams {
+  const float* tpart_o;     // [T*Hq, S, D]
+  const float* tpart_lse;   // [T*Hq, S]
+  const int32_t* query_start_loc;  // [B+1]
+  void* out;                // [T, Hq, D]
+  float* lse;               // [T, Hq] or null
+  int32_t num_seqs, num_q_heads, num_kv_heads;
+  int32_t q_tile, decode_rows_apart, tile_splits, out_f32;
 };
 
 // Launchers: return hipSuccess or the launch error.  Shapes were checked.
 hipError_t launch_decode(const DecodeParams& p, int group, int waves, bool fused,
                          hipStream_t stream);
+// Even-work decode grid of nw workgroups (separate merge only).
+hipError_t launch_decode_even(const DecodeParams& p, int group, int waves, int nw,
+                              hipStream_t stream);
+// Workgroups of the even-work decode kernel that fit on the device at once.
+int decode_even_resident(int group, int waves);
 // Prefill tiles (nx x Hkv workgroups) and n_dec decode workgroups (split x
 // Hkv x B, for the single-token sequences of a mixed batch) in one launch.
 hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
                           int n_dec, bool precise_p, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream);
 
 }  // namespace pa

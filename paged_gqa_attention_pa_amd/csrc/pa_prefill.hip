@@ -3,8 +3,9 @@
 // may contain single-token (decode) sequences, split-KV decode workgroups for
 // them (decode_body, pa_decode_body.h), so a mixed serving batch is one
 // launch (plus the LSE merge of the decode rows' splits).  Workgroup ids
-// [0, nx*Hkv) are prefill tiles, the rest (split, kv head, sequence) decode
-// work; both share one LDS buffer.
+// [0, nx*tile_splits*Hkv) are prefill tiles, the rest (split, kv head, sequence) decode
+// work; both share one LDS buffer.  With tile_splits > 1 the tiles write
+// partials, merged afterwards by tile_merge_kernel (pa_reduce.hip).
 #include "pa_decode_body.h"
 #include "pa_prefill_body.h"
 
@@ -42,7 +43,7 @@ template <int G, bool PRECISE>
 __global__ __launch_bounds__(kThreads, 2) void unified_kernel(PrefillParams pp, DecodeParams dp,
                                                               int nx) {
   __shared__ __attribute__((aligned(16))) char smem[unified_smem_bytes<G>()];
-  const int n_pre = nx * pp.num_kv_heads;
+  const int n_pre = nx * pp.num_kv_heads * pp.tile_splits;
   const int id = blockIdx.x;
   if (id < n_pre) {
     prefill_body<G, PRECISE>(pp, id, nx, smem);
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kThreads, 2) void unified_kernel(PrefillParams pp, 
 template <bool PRECISE>
 hipError_t launch_t(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
                     int n_dec, hipStream_t stream) {
-  const dim3 grid((unsigned)(nx * pp.num_kv_heads + n_dec));
+  const dim3 grid((unsigned)(nx * pp.num_kv_heads * pp.tile_splits + n_dec));
   const dim3 block(kThreads);
   switch (group) {
     case 1: hipLaunchKernelGGL((unified_kernel<1, PRECISE>), grid, block, 0, stream, pp, dp, nx); break;

@@ -24,6 +24,10 @@
 // so a chunk attends to its cached prefix in full).  The grid is static:
 // x runs over a host bound on query tiles; each workgroup finds its
 // sequence by a scan of query_start_loc and surplus workgroups exit.
+// With tile_splits = S > 1 the tile's key tiles are dealt out in S
+// contiguous runs (the parallel tiled softmax of the five-step list applied
+// to a query tile), each run writes normalised partials and their lse, and
+// tile_merge_kernel combines them by log-sum-exp.
 #pragma once
 
 #include "pa_device.h"
@@ -93,19 +97,22 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool 
 constexpr int kPrefillSmemBytes =
     kBufs * kKvTile * kLdsStride * 2 + kBufs * kHeadDim * kVtStride * 2 + kPageCache * 4;
 
-// One workgroup of kThreads threads: query tile / KV head number `id` of the
-// 1-D prefill grid (nx tiles x Hkv).  smem: kPrefillSmemBytes, 16-byte aligned.
+// One workgroup of kThreads threads: query tile / split / KV head number `id`
+// of the 1-D prefill grid (nx tiles x tile_splits x Hkv).  smem:
+// kPrefillSmemBytes, 16-byte aligned.
 template <int G, bool PRECISE>
 __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int nx,
                                              char* smem) {
   constexpr int D = kHeadDim;
   constexpr int QT = kRows / G;
-  // 1-D grid: id -> (kv head, query tile).  Consecutive ids go to different
-  // XCDs, so with Hkv = 8 each XCD serves one KV head and its K/V stay in
-  // that XCD's L2.  Query tiles run from the last (heaviest under the causal
-  // mask) to the first.
+  // 1-D grid: id -> (kv head, split, query tile).  Consecutive ids go to
+  // different XCDs, so with Hkv = 8 each XCD serves one KV head and its K/V
+  // stay in that XCD's L2.  Query tiles run from the last (heaviest under the
+  // causal mask) to the first.
   const int g = id % p.num_kv_heads;
-  const int x = nx - 1 - id / p.num_kv_heads;
+  const int nsplit = p.tile_splits;
+  const int split = (id / p.num_kv_heads) % nsplit;
+  const int x = nx - 1 - id / (p.num_kv_heads * nsplit);
   int s, qtile;
   if (!find_tile(p.query_start_loc, p.num_seqs, QT, x, p.decode_rows_apart != 0, &s, &qtile))
     return;
@@ -129,7 +136,16 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // below it need no mask
   const int wave_limit = p.causal ? min(L, L - qlen + tok0 + (32 * wave) / G + 1) : L;
   const int kv_end = p.causal ? min(L, L - qlen + tok0 + ntok) : L;
-  const int nkv = kv_end > 0 ? (kv_end + kKvTile - 1) / kKvTile : 0;
+  const int nkv_all = kv_end > 0 ? (kv_end + kKvTile - 1) / kKvTile : 0;
+  // this workgroup's run of key tiles [j0, j0 + nkv)
+  const int per = nsplit > 1 ? (nkv_all + nsplit - 1) / nsplit : nkv_all;
+  const int j0 = min(nkv_all, split * per);
+  const int nkv = min(nkv_all - j0, per);
+  const int64_t orow = (int64_t)(q0 + qi) * p.num_q_heads + g * G + h;
+  if (nsplit > 1 && nkv <= 0) {  // empty run: weight zero in the merge
+    if (row_valid && half == 0) p.tpart_lse[orow * nsplit + split] = kNegInf;
+    return;
+  }
 
   // Q^T operand: lane holds Q[row][16ks + 8*half .. +8] for ks = 0..7.
   bf16x8 qb[8];
@@ -150,39 +166,42 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
 
   // Tile loader: threads 0..255 stage K, threads 256..511 stage V; thread t
   // (mod 256) handles keys 2*(t%16), 2*(t%16)+1 (same page) and dims
-  // 8*((t%256)/16) .. +7.
+  // 8*((t%256)/16) .. +7.  Loads are unconditional (a key past the context
+  // reads a valid page and its V row is zeroed when stored), so no load sits
+  // under a branch and the compiler keeps them in flight across the loop.
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
   const bool v_side = tid >= 256;
   const uint16_t* src = (v_side ? p.v_pool : p.k_pool) + (int64_t)g * p.stride_head;
   const int kp = tid & 15, dc = (tid & 255) >> 4;
-  uint4 reg[2];
-  // The sequence's page ids, staged in LDS once, keep the block-table lookup
-  // off each tile's load path; blocks past the staged window read the table.
+  // Page ids of the current window of key tiles, staged in LDS, keep the
+  // block-table lookup off each tile's load path.  Entries past the
+  // context hold page 0 (never used: those keys are masked and zeroed).
   int* pg_lds = reinterpret_cast<int*>(smem + kBufs * kKvTile * kLdsStride * 2 +
                                        kBufs * D * kVtStride * 2);
-  {
-    // every key load_tile reads: below L and inside the nkv tiles
-    const int keys = min(L, nkv * kKvTile);
-    const int npg = min((keys + kPage - 1) / kPage, kPageCache);
-    for (int i = tid; i < npg; i += kThreads) pg_lds[i] = bt[i];
-    __syncthreads();
-  }
-  auto load_tile = [&](int j) {
-    const int key = j * kKvTile + 2 * kp;
-    const int blk = key / kPage;
-    const int64_t page = key < L ? (blk < kPageCache ? pg_lds[blk] : bt[blk]) : 0;
+  constexpr int kWinTiles = kPageCache * kPage / kKvTile;
+  const int nblk = (L + kPage - 1) / kPage;  // valid block-table entries
+  int win0 = 0;                              // first key tile of the window
+  // tile t of the window -> two 16-byte loads into r
+  auto load_tile = [&](int t, uint4 (&r)[2]) {
+    const int key = (win0 + t) * kKvTile + 2 * kp;
+    const int64_t page = pg_lds[(win0 + t) * (kKvTile / kPage) + (2 * kp) / kPage -
+                                win0 * (kKvTile / kPage)];
     const int64_t off = page * p.stride_page + (int64_t)(key % kPage) * p.stride_token + 8 * dc;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    reg[0] = key < L ? ld16(src + off) : z;
-    reg[1] = key + 1 < L ? ld16(src + off + p.stride_token) : z;
+    r[0] = ld16(src + off);
+    r[1] = ld16(src + off + p.stride_token);
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int t, int buf, const uint4 (&r)[2]) {
+    const int key = (win0 + t) * kKvTile + 2 * kp;
     if (!v_side) {
-      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp) * kLdsStride + 8 * dc]) = reg[0];
-      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp + 1) * kLdsStride + 8 * dc]) = reg[1];
+      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp) * kLdsStride + 8 * dc]) = r[0];
+      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp + 1) * kLdsStride + 8 * dc]) = r[1];
     } else {
-      const uint32_t a[4] = {reg[0].x, reg[0].y, reg[0].z, reg[0].w};
-      const uint32_t b[4] = {reg[1].x, reg[1].y, reg[1].z, reg[1].w};
+      // V rows past the context are zeroed: stale data (even NaN) must not
+      // reach O through a zero weight
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 va = key < L ? r[0] : z, vb = key + 1 < L ? r[1] : z;
+      const uint32_t a[4] = {va.x, va.y, va.z, va.w};
+      const uint32_t b[4] = {vb.x, vb.y, vb.z, vb.w};
       uint32_t* vt = reinterpret_cast<uint32_t*>(&vt_lds[buf][0]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -214,37 +233,27 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     for (int e = 0; e < 16; ++e) o[mt][e] = 0.f;
   float m = kNegInf, lsum = 0.f;
   const float c = p.scale_log2;  // > 0 (checked on the host)
-
-#pragma unroll
-  for (int j = 0; j < kBufs - 1; ++j)
-    if (j < nkv) {
-      load_tile(j);
-      store_tile(j);
-    }
-  __syncthreads();
-  if (kBufs - 1 < nkv) load_tile(kBufs - 1);
   f32x16 st_cur, st_next;
-  if (nkv > 0) qk(0, st_cur);
 
-  for (int j = 0; j < nkv; ++j) {
-    const int buf = j % kBufs;
-    if (j + 1 < nkv) qk((j + 1) % kBufs, st_next);  // MFMA pipe, overlaps the softmax below
-
-    // Register e holds key 8*(e/4) + 4*half + e%4 of tile j, row n; the
+  // One key tile: softmax of tile jg (its S^T in st_cur, its V^T in buffer
+  // buf) and O^T += V^T P^T.
+  auto softmax_pv = [&](int jg, int buf) {
+    // Register e holds key 8*(e/4) + 4*half + e%4 of the tile, row n; the
     // log2-domain logit is c*S (c > 0, so the max can be taken on S).
-    float smax = kNegInf;
-    const bool full = j * kKvTile + kKvTile <= wave_limit;  // no key of the tile masked
+    const bool full = jg * kKvTile + kKvTile <= wave_limit;  // no key of the tile masked
     if (!full) {
-      const int kbase = j * kKvTile + 4 * half;
+      const int kbase = jg * kKvTile + 4 * half;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kbase + 8 * (e >> 2) + (e & 3);
         st_cur[e] = (key < key_limit) ? st_cur[e] : kNegInf;
       }
     }
+    float smax = kNegInf;
 #pragma unroll
     for (int e = 0; e < 16; ++e) smax = fmaxf(smax, st_cur[e]);
-    const float tmax = fmaxf(smax, shfl_xor(smax, 32)) * c;
+    const f32x2 hm = halves(smax);
+    const float tmax = fmaxf(hm[0], hm[1]) * c;
     const bool need = tmax > m + kLazyThreshold;
     if (wave_any(need)) {
       const float m_new = need ? tmax : m;
@@ -263,10 +272,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     for (int e = 0; e < 16; e += 2) {
       const float p0 = fast_exp2(fmaf(st_cur[e], c, neg_m));
       const float p1 = fast_exp2(fmaf(st_cur[e + 1], c, neg_m));
-      psum += p0 + p1;
       pk[e >> 1] = pack_bf16x2(p0, p1);
       if constexpr (PRECISE) {
+        psum += p0 + p1;
         pl[e >> 1] = pack_bf16x2(p0 - bf16lo(pk[e >> 1]), p1 - bf16hi(pk[e >> 1]));
+      } else {
+        // the row sum of the weights the MFMA uses (P rounded to bf16)
+        psum = add_bf16x2(pk[e >> 1], psum);
       }
     }
     lsum += psum;
@@ -292,18 +304,67 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
           o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbl, o[mt], 0, 0, 0);
       }
     }
-    // Tile j+2 goes to the buffer tile j-1 used (its last reads were before
-    // the previous barrier); its global loads were issued an iteration ago.
-    if (j + kBufs - 1 < nkv) store_tile((j + kBufs - 1) % kBufs);
+  };
+
+  // The run [j0, j0 + nkv) in windows of at most kWinTiles key tiles (one
+  // LDS page-id window each).  Inside a window, three LDS buffers: while tile
+  // j is finished (softmax, P.V), the S^T MFMAs of tile j+1 already run,
+  // tile j+2 is stored from registers and tile j+3's global loads are in
+  // flight (two register sets, so a tile's loads have two iterations to
+  // land); one barrier per tile.
+  for (int wbeg = 0; wbeg < nkv; wbeg += kWinTiles) {
+    const int nw = min(kWinTiles, nkv - wbeg);
+    win0 = j0 + wbeg;
+    {
+      const int b0 = win0 * (kKvTile / kPage);
+      const int nb = nw * (kKvTile / kPage);
+      for (int i = tid; i < nb; i += kThreads) pg_lds[i] = (b0 + i < nblk) ? bt[b0 + i] : 0;
+      __syncthreads();
+    }
+    uint4 ra[2], rb[2];
+    load_tile(0, ra);
+    load_tile(min(1, nw - 1), rb);
+    store_tile(0, 0, ra);
+    if (nw > 1) store_tile(1, 1, rb);
     __syncthreads();
-    if (j + kBufs < nkv) load_tile(j + kBufs);
-    st_cur = st_next;
+    load_tile(min(2, nw - 1), ra);
+    qk(0, st_cur);
+    // iteration j: ra/rb alternate as "tile j+2 (loaded)" / "tile j+3 (loading)"
+    auto step = [&](int j, uint4 (&cur)[2], uint4 (&nxt)[2]) {
+      if (j + 1 < nw) qk((j + 1) % kBufs, st_next);  // MFMA pipe, overlaps the softmax below
+      load_tile(min(j + 3, nw - 1), nxt);
+      softmax_pv(win0 + j, j % kBufs);
+      // tile j+2 goes to the buffer tile j-1 used (its last reads were before
+      // the previous barrier)
+      if (j + 2 < nw) store_tile(j + 2, (j + 2) % kBufs, cur);
+      __syncthreads();
+      st_cur = st_next;
+    };
+    for (int j = 0; j < nw; j += 2) {
+      step(j, ra, rb);
+      if (j + 1 < nw) step(j + 1, rb, ra);
+    }
   }
 
-  const float l = lsum + shfl_xor(lsum, 32);
+  const f32x2 lh = halves(lsum);
+  const float l = lh[0] + lh[1];
   if (!row_valid) return;
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  const int64_t orow = (int64_t)(q0 + qi) * p.num_q_heads + g * G + h;
+  const float row_lse = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
+  if (nsplit > 1) {  // partial of this run: normalised O and its lse
+    float* dst = p.tpart_o + (orow * nsplit + split) * D;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int d = 32 * mt + 8 * rb + 4 * half;
+        *reinterpret_cast<float4*>(dst + d) =
+            make_float4(o[mt][4 * rb] * inv, o[mt][4 * rb + 1] * inv, o[mt][4 * rb + 2] * inv,
+                        o[mt][4 * rb + 3] * inv);
+      }
+    if (half == 0) p.tpart_lse[orow * nsplit + split] = row_lse;
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -319,7 +380,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
             make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
       }
     }
-  if (p.lse && half == 0) p.lse[orow] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
+  if (p.lse && half == 0) p.lse[orow] = row_lse;
 }
 
 }  // namespace prefill_detail

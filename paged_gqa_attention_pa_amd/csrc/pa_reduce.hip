@@ -13,6 +13,7 @@
 // the groups are summed through LDS.
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_prefill_body.h"
 
 namespace pa {
 
@@ -49,9 +50,28 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
     if (p.query_start_loc[s + 1] - q0 != 1) return;
     orow = (int64_t)q0 * p.num_q_heads + row % p.num_q_heads;
   }
-  const int S = p.num_splits;
+  const int stride = p.num_splits;  // partial slots per row
+  int S = stride;                   // slots in use
   const int D = p.head_dim;
-  const float* lse_row = p.part_lse + (int64_t)row * S;
+  if (p.piece_counts) {
+    // even-work decode grid: an empty context has no pieces (O = 0,
+    // lse = -inf); a unit of one piece was written directly
+    const int b = row / p.num_q_heads;
+    const int u = b * (p.num_q_heads / p.group) + (row % p.num_q_heads) / p.group;
+    if (p.context_lens[b] <= 0) {
+      for (int d = tid; d < D; d += kThreads) {
+        if (p.out_f32)
+          reinterpret_cast<float*>(p.out)[orow * D + d] = 0.f;
+        else
+          reinterpret_cast<uint16_t*>(p.out)[orow * D + d] = 0;
+      }
+      if (p.lse && tid == 0) p.lse[orow] = kNegInf;
+      return;
+    }
+    S = min(p.piece_counts[u], stride);
+    if (S <= 1) return;
+  }
+  const float* lse_row = p.part_lse + (int64_t)row * stride;
 
   float M = kNegInf;
   for (int k = tid; k < S; k += kThreads) {
@@ -80,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
     const int grp = tid / chunk;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     if (grp < groups && M != kNegInf) {
-      const float* src = p.part_o + (int64_t)row * S * D + 4 * item;
+      const float* src = p.part_o + (int64_t)row * stride * D + 4 * item;
       // Eight independent loads per batch; an empty split (weight 0) may hold
       // stale values, so its contribution is selected away, not multiplied.
       int k = grp;
@@ -131,7 +151,107 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
   if (p.lse && tid == 0) p.lse[orow] = (M == kNegInf) ? kNegInf : M + fast_log2(wsum) * kLn2;
 }
 
+// Merge of split query tiles.  Workgroup (kv head g, tile x) finds its tile
+// as the prefill workgroups do, so rows of single-token sequences that ran as
+// decode workgroups are never touched.  Its rows r = 0 .. ntok*G-1 (token
+// r / G, head g*G + r % G) are spread over the eight wavefronts; 32 lanes
+// cover one row's 128 dims with 16-byte loads, so a wavefront merges two
+// rows per step and keeps four steps (eight rows) of loads in flight.
+constexpr int kMergeRowsPerIter = 8;
+
+template <int S>
+__global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(TileMergeParams p,
+                                                                             int nx) {
+  using prefill_detail::find_tile;
+  constexpr int D = kHeadDim;
+  const int g = blockIdx.x % p.num_kv_heads;
+  const int x = nx - 1 - blockIdx.x / p.num_kv_heads;
+  int s, qtile;
+  if (!find_tile(p.query_start_loc, p.num_seqs, p.q_tile, x, p.decode_rows_apart != 0, &s,
+                 &qtile))
+    return;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int q0 = p.query_start_loc[s];
+  const int qlen = p.query_start_loc[s + 1] - q0;
+  const int tok0 = qtile * p.q_tile;
+  const int nrows = min(p.q_tile, qlen - tok0) * G;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane >> 5, dl = lane & 31;
+  const int rows_per_wave = (nrows + prefill_detail::kWaves - 1) / prefill_detail::kWaves;
+  const int r_begin = wave * rows_per_wave;
+  const int r_end = min(nrows, r_begin + rows_per_wave);
+  for (int r0 = r_begin; r0 < r_end; r0 += kMergeRowsPerIter) {
+    int64_t orow[kMergeRowsPerIter / 2];
+    bool valid[kMergeRowsPerIter / 2];
+    float M[kMergeRowsPerIter / 2];
+#pragma unroll
+    for (int u = 0; u < kMergeRowsPerIter / 2; ++u) {
+      const int r = r0 + 2 * u + sub;
+      valid[u] = r < r_end;
+      const int rr = valid[u] ? r : r_begin;
+      orow[u] = (int64_t)(q0 + tok0 + rr / G) * p.num_q_heads + g * G + rr % G;
+      M[u] = kNegInf;
+    }
+    float lse_v[kMergeRowsPerIter / 2][S];
+    float4 v[kMergeRowsPerIter / 2][S];
+#pragma unroll
+    for (int u = 0; u < kMergeRowsPerIter / 2; ++u)
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        lse_v[u][k] = p.tpart_lse[orow[u] * S + k];
+        v[u][k] = *reinterpret_cast<const float4*>(p.tpart_o + (orow[u] * S + k) * D + 4 * dl);
+        M[u] = fmaxf(M[u], lse_v[u][k]);
+      }
+#pragma unroll
+    for (int u = 0; u < kMergeRowsPerIter / 2; ++u) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float wsum = 0.f;
+      if (M[u] != kNegInf) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+          // an empty run (lse -inf, and stale O) gets weight 0 by select
+          const bool on = lse_v[u][k] != kNegInf;
+          const float w = on ? fast_exp2((lse_v[u][k] - M[u]) * kLog2e) : 0.f;
+          wsum += w;
+          acc.x = fmaf(w, on ? v[u][k].x : 0.f, acc.x);
+          acc.y = fmaf(w, on ? v[u][k].y : 0.f, acc.y);
+          acc.z = fmaf(w, on ? v[u][k].z : 0.f, acc.z);
+          acc.w = fmaf(w, on ? v[u][k].w : 0.f, acc.w);
+        }
+      }
+      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+      acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
+      if (!valid[u]) continue;
+      const int64_t off = orow[u] * D + 4 * dl;
+      if (p.out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) = acc;
+      } else {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + off) =
+            make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+      }
+      if (p.lse && dl == 0)
+        p.lse[orow[u]] = (M[u] == kNegInf) ? kNegInf : M[u] + fast_log2(wsum) * kLn2;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream) {
+  if (nx <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(nx * p.num_kv_heads)), block(prefill_detail::kThreads);
+  switch (p.tile_splits) {
+    case 2: hipLaunchKernelGGL(tile_merge_kernel<2>, grid, block, 0, stream, p, nx); break;
+    case 3: hipLaunchKernelGGL(tile_merge_kernel<3>, grid, block, 0, stream, p, nx); break;
+    case 4: hipLaunchKernelGGL(tile_merge_kernel<4>, grid, block, 0, stream, p, nx); break;
+    case 5: hipLaunchKernelGGL(tile_merge_kernel<5>, grid, block, 0, stream, p, nx); break;
+    case 6: hipLaunchKernelGGL(tile_merge_kernel<6>, grid, block, 0, stream, p, nx); break;
+    case 7: hipLaunchKernelGGL(tile_merge_kernel<7>, grid, block, 0, stream, p, nx); break;
+    case 8: hipLaunchKernelGGL(tile_merge_kernel<8>, grid, block, 0, stream, p, nx); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {
   if (p.rows == 0) return hipSuccess;

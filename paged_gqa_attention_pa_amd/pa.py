@@ -36,7 +36,7 @@ class Problem(ctypes.Structure):
 class Tiles(ctypes.Structure):
     _fields_ = [("kv_tile", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("waves_per_wg", ctypes.c_int32), ("q_tokens_per_tile", ctypes.c_int32),
-                ("variant", ctypes.c_int32)]
+                ("variant", ctypes.c_int32), ("tile_splits", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -64,6 +64,18 @@ def test_select_tiles_decode_and_prefill(lib):
     st, t, ws = _select(lib, _problem(max_query_len=2048, total_query_tokens=8192,
                                       max_context_len=3072))
     assert st == pa.PA_OK and t.q_tokens_per_tile == 64 and t.num_splits == 1 and ws == 0
+    assert t.tile_splits == 1
+    # two long-prefix chunks alone: tiles are split, and the workspace holds
+    # their partials (fp32 [T*Hq, ts, 128] + lse)
+    T = 2 * 512
+    st, t, ws = _select(lib, _problem(num_seqs=2, max_query_len=512, total_query_tokens=T,
+                                      max_context_len=4608, max_blocks_per_seq=512))
+    assert st == pa.PA_OK and t.tile_splits == 2 and t.num_splits == 1
+    assert ws >= T * 32 * 2 * 129 * 4
+    # the same chunks beside decode rows: decode splits, no tile split
+    st, t, ws = _select(lib, _problem(num_seqs=18, max_query_len=512, total_query_tokens=T + 16,
+                                      max_context_len=16384, max_blocks_per_seq=1024))
+    assert st == pa.PA_OK and t.tile_splits == 1 and t.num_splits > 1
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -87,6 +99,15 @@ def test_select_tiles_rejects(lib, field, value, status):
     assert st == status
 
 
+@pytest.mark.parametrize("ts", [-1, 9])
+def test_workspace_size_rejects_tile_splits(lib, ts):
+    pb = _problem(max_query_len=64, total_query_tokens=256)
+    t = pa.Tiles(32, 1, 8, 64, 0, ts)
+    ws = ctypes.c_size_t(0)
+    assert lib.pa_workspace_size(ctypes.byref(pb), ctypes.byref(t), ctypes.byref(ws)) == \
+        pa.PA_ERR_INVALID_ARG
+
+
 def test_compute_calls_reject_before_launch(lib):
     pb = _problem()
     t = pa.Tiles(16, 1, 4, 1, 0)
@@ -103,10 +124,19 @@ def test_compute_calls_reject_before_launch(lib):
     t2 = pa.Tiles(16, 8, 4, 1, 0)
     assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t2), fake, fake, fake, fake, fake, fake,
                          nul, nul, 0, nul) == pa.PA_ERR_WORKSPACE
+    # even-work grid without the separate merge
+    t5 = pa.Tiles(16, 8, 4, 1, 4)
+    assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t5), fake, fake, fake, fake, fake, fake,
+                         nul, fake, 1 << 30, nul) == pa.PA_ERR_INVALID_ARG
     # too many splits
     t3 = pa.Tiles(16, 100000, 4, 1, 0)
     assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t3), fake, fake, fake, fake, fake, fake,
                          nul, nul, 0, nul) == pa.PA_ERR_INVALID_ARG
+    # split query tiles without the workspace for their partials
+    pt = _problem(max_query_len=64, total_query_tokens=256)
+    t4 = pa.Tiles(32, 1, 8, 64, 0, 2)
+    assert lib.pa_prefill(ctypes.byref(pt), ctypes.byref(t4), fake, fake, fake, fake, fake, fake,
+                          fake, nul, nul, 0, nul) == pa.PA_ERR_WORKSPACE
     # prefill without query_start_loc
     pp = _problem(max_query_len=64, total_query_tokens=256)
     assert lib.pa_prefill(ctypes.byref(pp), ctypes.byref(t), fake, nul, fake, fake, fake, fake,

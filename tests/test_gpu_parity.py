@@ -57,14 +57,31 @@ def run_decode(b, out_dtype=torch.bfloat16, splits=None, with_lse=True, waves=No
     return out, lse
 
 
-def run_prefill(b, out_dtype=torch.bfloat16, with_lse=True):
+def run_prefill(b, out_dtype=torch.bfloat16, with_lse=True, tile_splits=None,
+                stale_workspace=False):
+    """pa_prefill on a batch; tile_splits forces the query-tile split count,
+    stale_workspace fills the workspace with NaN first (pa_prefill needs no
+    zeroed counters: its decode rows always use the separate merge)."""
     lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=b.q.device) if with_lse else None
     qsl = b.query_start_loc
     if qsl is None:
         qsl = torch.arange(b.num_seqs + 1, dtype=torch.int32, device=b.q.device)
+    max_q = max(b.max_query_len, 1)
+    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, b.spec.scale,
+                         b.max_context_len, max_q, causal=b.spec.causal, out_dtype=out_dtype)
+    tiles, _ = pa.select_tiles(pb)
+    if tile_splits is not None:
+        tiles.tile_splits = tile_splits
+    ws = pa.workspace_size(pb, tiles)
+    workspace = None
+    if ws:
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=b.q.device)
+        if stale_workspace:
+            workspace.fill_(0xFF)  # every fp32 slot reads as NaN
     out = pa.prefill(b.q, qsl, b.k_pool, b.v_pool, b.block_tables, b.context_lens,
-                     b.spec.scale, b.max_context_len, max(b.max_query_len, 1),
-                     causal=b.spec.causal, out_dtype=out_dtype, lse=lse)
+                     b.spec.scale, b.max_context_len, max_q,
+                     causal=b.spec.causal, out_dtype=out_dtype, lse=lse, tiles=tiles,
+                     workspace=workspace, problem=pb)
     torch.cuda.synchronize()
     return out, lse
 
@@ -107,13 +124,16 @@ DECODE_CASES = [
     ("g2", [100, 33, 257], 16, 8),
     ("g8", [100, 33, 257], 32, 4),
     ("g16", [100, 33, 257], 16, 1),
+    ("skewed", [5000, 0, 1, 17, 3000, 0, 64, 2049, 16, 700], 32, 8),
 ]
+
+MERGE_VARIANT = {"fused": 0, "separate": 2, "even": 6}
 
 
 @pytest.mark.parametrize("name,ctx,hq,hkv", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
 @pytest.mark.parametrize("splits", [None, 1, 3, 64])
 @pytest.mark.parametrize("waves", [4, 8])
-@pytest.mark.parametrize("merge", ["fused", "separate"])
+@pytest.mark.parametrize("merge", ["fused", "separate", "even"])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_decode_small(dev, name, ctx, hq, hkv, splits, waves, merge, out_dtype):
     if hq // hkv == 16 and waves == 8:
@@ -122,8 +142,7 @@ def test_decode_small(dev, name, ctx, hq, hkv, splits, waves, merge, out_dtype):
     spec = workloads.small_spec(f"dec_{name}", seed=100 + len(ctx) + hq, contexts=ctx,
                                 queries=[1] * len(ctx), num_q_heads=hq, num_kv_heads=hkv)
     b = workloads.generate(spec, dev)
-    out, lse = run_decode(b, out_dtype, splits, waves=waves,
-                          variant=2 if merge == "separate" else 0)
+    out, lse = run_decode(b, out_dtype, splits, waves=waves, variant=MERGE_VARIANT[merge])
     compare(b, out, lse, label=f"decode {name} S={splits} W={waves} {merge}")
 
 
@@ -146,6 +165,28 @@ def test_decode_workspace_reuse(dev):
                 first = out.clone()
             else:
                 assert torch.equal(out, first), "same call, different bits"
+
+
+@pytest.mark.parametrize("splits", [2, 8, 64])
+def test_decode_even_grid_stale_workspace(dev, splits):
+    """Even-work grid over a workspace holding garbage (0xFF bytes: NaN
+    partials, piece counts of -1) from an earlier user: every slot and count
+    it reads is written by this call, or the row is empty or single-piece."""
+    log(f"[decode even grid, stale workspace, S={splits}]")
+    spec = workloads.small_spec("even_stale", seed=13, contexts=[4000, 0, 33, 1, 2500, 16, 0, 900],
+                                queries=[1] * 8, pool_slack=20)
+    b = workloads.generate(spec, dev)
+    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                         b.max_context_len, 1, out_dtype=torch.float32)
+    t, _ = pa.select_tiles(pb)
+    t.num_splits, t.variant = splits, 6
+    ws = torch.full((pa.workspace_size(pb, t),), 0xFF, dtype=torch.uint8, device=dev)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=dev)
+    out = pa.decode(b.q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, spec.scale,
+                    b.max_context_len, out_dtype=torch.float32, lse=lse, tiles=t, workspace=ws,
+                    problem=pb)
+    torch.cuda.synchronize()
+    compare(b, out, lse, label=f"even stale S={splits}")
 
 
 def test_decode_logit_stress(dev):
@@ -251,6 +292,37 @@ def test_prefill_small(dev, name, ctx, ql, causal, out_dtype):
     compare(b, out, lse, label=f"prefill {name}")
 
 
+TILE_SPLIT_CASES = [
+    # (name, contexts, query lens, causal): runs long enough to split, runs of
+    # one tile or none, decode rows beside split tiles, no causal mask
+    ("long_prefix", [2100, 1500], [300, 200], True),
+    ("short_runs", [40, 64, 65, 200], [40, 64, 65, 129], True),
+    ("decode_rows_first", [900, 40, 2600, 513], [1, 1, 100, 200], True),
+    ("noncausal", [3000, 50], [100, 7], False),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql,causal", TILE_SPLIT_CASES,
+                         ids=[c[0] for c in TILE_SPLIT_CASES])
+@pytest.mark.parametrize("ts", [2, 3, 8])
+def test_prefill_tile_splits(dev, name, ctx, ql, causal, ts):
+    """Query tiles whose keys are cut into ts runs, merged by log-sum-exp,
+    over a NaN-filled workspace, in both output precisions."""
+    log(f"[prefill tile splits {name} ts={ts}]")
+    spec = workloads.small_spec(f"pts_{name}", seed=700 + ts + sum(ql), contexts=ctx,
+                                queries=ql, causal=causal, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    T = sum(ql) * spec.num_q_heads
+    rows = None
+    if T > 4096:  # sample rows, always including the first and last of each sequence
+        rng = np.random.default_rng(ts)
+        rows = np.unique(np.concatenate([rng.choice(T, 2048, replace=False),
+                                         np.array([0, T - 1])]))
+    for dt in (torch.bfloat16, torch.float32):
+        out, lse = run_prefill(b, dt, tile_splits=ts, stale_workspace=True)
+        compare(b, out, lse, rows=rows, label=f"tile splits {name} ts={ts} {dt}")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 4), (16, 1)])
 def test_prefill_group_sizes(dev, hq, hkv):
     log(f"[prefill G={hq // hkv}]")
@@ -266,15 +338,16 @@ def test_prefill_dominant_logit_bitexact(dev):
     L, q = 300, 40
     tstars = [0, 31, 32, 200, 259]  # all <= L - q, so every row of the chunk sees t*
     b = _dominant_batch(dev, tstars, L, prefill_q=q)
-    for dt in (torch.bfloat16, torch.float32):
-        out, _ = run_prefill(b, dt)
+    for dt, ts in ((torch.bfloat16, 1), (torch.float32, 1), (torch.bfloat16, 3),
+                   (torch.float32, 8)):
+        out, _ = run_prefill(b, dt, tile_splits=ts)
         for s, t in enumerate(tstars):
             page = int(b.block_tables[s, t // 16])
             want = b.v_pool[page, t % 16].repeat_interleave(4, dim=0).to(dt)
             got = out[s * q:(s + 1) * q]
             ok = (torch.equal(got.view(torch.int16), want.view(torch.int16).expand_as(got))
                   if dt == torch.bfloat16 else torch.equal(got, want.expand_as(got)))
-            assert ok, f"seq {s} t*={t} {dt}"
+            assert ok, f"seq {s} t*={t} {dt} tile_splits={ts}"
 
 
 def test_prefill_page_permutation_and_nan_bitexact(dev):
@@ -288,6 +361,12 @@ def test_prefill_page_permutation_and_nan_bitexact(dev):
     o3, l3 = run_prefill(bz, torch.float32)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # the same with split query tiles (and stale partial slots)
+    s1, m1 = run_prefill(b, torch.float32, tile_splits=3, stale_workspace=True)
+    s2, m2 = run_prefill(_permuted(b), torch.float32, tile_splits=3, stale_workspace=True)
+    s3, m3 = run_prefill(bz, torch.float32, tile_splits=3)
+    assert torch.equal(s1, s2) and torch.equal(m1, m2)
+    assert torch.equal(s1, s3) and torch.equal(m1, m3)
 
 
 # ---------------------------------------------------------------- reduce ----
