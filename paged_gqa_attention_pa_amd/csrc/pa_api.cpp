@@ -154,9 +154,13 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
                        ? pa::table_decode_splits(problem->num_seqs, problem->num_kv_heads,
                                                  problem->max_context_len)
                        : 1;
-    // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18
+    // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18;
+    // single-token sequences take the decode table's grid choice
     t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
-                pa::kVariantSeparateMerge;
+                pa::kVariantSeparateMerge |
+                (pa::table_decode_variant(problem->num_seqs, problem->num_kv_heads,
+                                          problem->max_context_len) &
+                 pa::kVariantEvenWork);
     // Split query tiles only in batches without single-token sequences:
     // measured on gfx950, decode workgroups already use the CUs that a few
     // long query tiles leave idle, and splitting the tiles then only adds
@@ -277,6 +281,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   // sequences take the prefill tiles
   const bool decode_rows = may_hold_decode_rows(problem) && G <= 8;
   const int S = decode_rows ? tiles->num_splits : 1;
+  const bool even = decode_rows && even_grid(tiles);
   const int TS = tile_splits_of(problem, tiles);
   const Workspace wl = workspace_layout(problem, tiles);
   if (wl.total > 0 && (!workspace || workspace_bytes < wl.total ||
@@ -329,11 +334,13 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.part_lse = nullptr;
   d.counters = nullptr;
   d.query_start_loc = query_start_loc;
+  d.piece_counts = nullptr;
   if (S > 1) {
     char* ws = static_cast<char*>(workspace);
     d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
     d.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
     d.counters = reinterpret_cast<int32_t*>(ws + wl.ctr_off);
+    if (even) d.piece_counts = reinterpret_cast<int32_t*>(ws + wl.cnt_off);
   }
   d.stride_page = p.stride_page;
   d.stride_token = p.stride_token;
@@ -342,21 +349,23 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.num_q_heads = problem->num_q_heads;
   d.num_kv_heads = problem->num_kv_heads;
   d.max_blocks = problem->max_blocks_per_seq;
-  d.num_splits = S;
+  d.num_splits = even ? S + 1 : S;
   const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
   d.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
   d.max_tiles = ntiles;
-  d.even_min_tiles = 0;
-  d.piece_counts = nullptr;
+  d.even_min_tiles = d.tiles_per_split;
   d.scale_log2 = scale_log2;
   d.out_f32 = out_f32;
 
   // static grid: sum over sequences of ceil(q_len / qt) <= ceil(T / qt) + B
   const int64_t nx = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
-  const int64_t n_dec =
-      decode_rows ? (int64_t)problem->num_seqs * problem->num_kv_heads * S : 0;
-  if (nx * problem->num_kv_heads * TS + n_dec > 0x7fffffff) return PA_ERR_UNSUPPORTED;
   const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
+  int64_t n_dec = decode_rows ? (int64_t)problem->num_seqs * problem->num_kv_heads * S : 0;
+  if (even) {
+    n_dec = pa::unified_resident(G, precise);
+    if (n_dec <= 0) return PA_ERR_HIP;
+  }
+  if (nx * problem->num_kv_heads * TS + n_dec > 0x7fffffff) return PA_ERR_UNSUPPORTED;
   if ((st = from_hip(pa::launch_prefill(p, d, G, (int)nx, (int)n_dec, precise, stream))) != PA_OK)
     return st;
   if (TS > 1) {
@@ -382,12 +391,12 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     r.out = out;
     r.lse = lse;
     r.rows = problem->num_seqs * problem->num_q_heads;
-    r.num_splits = S;
+    r.num_splits = d.num_splits;
     r.head_dim = problem->head_dim;
     r.out_f32 = out_f32;
     r.query_start_loc = query_start_loc;
     r.num_q_heads = problem->num_q_heads;
-    r.piece_counts = nullptr;
+    r.piece_counts = d.piece_counts;
     r.context_lens = context_lens;
     r.group = G;
     st = from_hip(pa::launch_reduce(r, stream));

@@ -109,6 +109,8 @@ int decode_even_resident(int group, int waves);
 // Hkv x B, for the single-token sequences of a mixed batch) in one launch.
 hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
                           int n_dec, bool precise_p, hipStream_t stream);
+// Workgroups of the unified prefill kernel that fit on the device at once.
+int unified_resident(int group, bool precise_p);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream);
 

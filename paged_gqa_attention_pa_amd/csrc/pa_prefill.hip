@@ -6,6 +6,8 @@
 // [0, nx*tile_splits*Hkv) are prefill tiles, the rest (split, kv head, sequence) decode
 // work; both share one LDS buffer.  With tile_splits > 1 the tiles write
 // partials, merged afterwards by tile_merge_kernel (pa_reduce.hip).
+#include <atomic>
+
 #include "pa_decode_body.h"
 #include "pa_prefill_body.h"
 
@@ -14,6 +16,7 @@ namespace pa {
 namespace {
 
 using decode_detail::decode_body;
+using decode_detail::decode_even_body;
 using decode_detail::decode_smem_floats;
 using prefill_detail::kPrefillSmemBytes;
 using prefill_detail::kThreads;
@@ -49,10 +52,14 @@ __global__ __launch_bounds__(kThreads, 2) void unified_kernel(PrefillParams pp, 
     prefill_body<G, PRECISE>(pp, id, nx, smem);
   } else if constexpr (decode_part_built<G>()) {
     const int d = id - n_pre;
-    const int split = d % dp.num_splits;
-    const int g = (d / dp.num_splits) % dp.num_kv_heads;
-    const int b = d / (dp.num_splits * dp.num_kv_heads);
-    decode_body<G, kDecodeWaves, false>(dp, split, g, b, reinterpret_cast<float*>(smem));
+    if (dp.piece_counts) {  // even-work grid over the single-token sequences
+      decode_even_body<G, kDecodeWaves>(dp, d, gridDim.x - n_pre, reinterpret_cast<float*>(smem));
+    } else {
+      const int split = d % dp.num_splits;
+      const int g = (d / dp.num_splits) % dp.num_kv_heads;
+      const int b = d / (dp.num_splits * dp.num_kv_heads);
+      decode_body<G, kDecodeWaves, false>(dp, split, g, b, reinterpret_cast<float*>(smem));
+    }
   }
 }
 
@@ -75,7 +82,37 @@ hipError_t launch_t(const PrefillParams& pp, const DecodeParams& dp, int group, 
   return hipGetLastError();
 }
 
+template <bool PRECISE>
+const void* unified_ptr(int group) {
+  switch (group) {
+    case 1: return reinterpret_cast<const void*>(&unified_kernel<1, PRECISE>);
+    case 2: return reinterpret_cast<const void*>(&unified_kernel<2, PRECISE>);
+    case 4: return reinterpret_cast<const void*>(&unified_kernel<4, PRECISE>);
+    case 8: return reinterpret_cast<const void*>(&unified_kernel<8, PRECISE>);
+    case 16: return reinterpret_cast<const void*>(&unified_kernel<16, PRECISE>);
+    default: return nullptr;
+  }
+}
+
 }  // namespace
+
+int unified_resident(int group, bool precise_p) {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs][5][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
+  const int cached = cache[dev][gi][precise_p].load(std::memory_order_relaxed);
+  if (cached > 0) return cached;
+  const void* k = precise_p ? unified_ptr<true>(group) : unified_ptr<false>(group);
+  int cus = 0, per_cu = 0;
+  if (!k || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess)
+    return 0;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  cache[dev][gi][precise_p].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
                           int n_dec, bool precise_p, hipStream_t stream) {
