@@ -27,6 +27,8 @@
  *                 page*kv_stride_page + slot*kv_stride_token
  *                 + kv_head*kv_stride_head + d   (d stride is 1)
  *                 K and V share the strides.  Default: [pages, P, Hkv, D].
+ *                 Each stride must be below 2^31 elements (PA_ERR_UNSUPPORTED
+ *                 otherwise).
  *   block_tables  int32 [B, max_blocks_per_seq]; entry b of row s is the
  *                 page holding logical tokens [b*P, (b+1)*P) of sequence s.
  *                 Entries past ceil(context_lens[s]/P) are never read.

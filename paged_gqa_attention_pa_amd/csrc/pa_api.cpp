@@ -39,6 +39,10 @@ pa_status check_problem(const pa_problem* pb) {
   if ((int64_t)pb->max_context_len > (int64_t)pb->max_blocks_per_seq * pb->page_size)
     return PA_ERR_INVALID_ARG;
   if (pb->head_dim != kHeadDim || pb->page_size != kPage) return PA_ERR_UNSUPPORTED;
+  // the kernels form page offsets as 32-bit byte strides times page ids
+  if (pb->kv_stride_page > 0x7fffffff || pb->kv_stride_token > 0x7fffffff ||
+      pb->kv_stride_head > 0x7fffffff)
+    return PA_ERR_UNSUPPORTED;
   if (!group_built(pb->num_q_heads / pb->num_kv_heads)) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }

@@ -15,10 +15,12 @@
 //   masked keys (past the context, or after the row's causal position) are
 //   removed by select.
 //   O^T += V^T P^T  v_mfma_f32_32x32x16_bf16; P (rounded to bf16) is already
-//                 in the B-operand layout the S^T result left it in; V^T is
-//                 gathered from LDS.  The precise variant splits P into a bf16
-//                 high part and a bf16 remainder (two MFMAs), leaving a
-//                 relative weight error of about 2^-18 instead of 2^-9.
+//                 in the B-operand layout the S^T result left it in; V stays
+//                 row-major in LDS and V^T comes out of ds_read_b64_tr_b16
+//                 (each 16-lane group transposes a 4-key x 16-dim block).
+//                 The precise variant splits P into a bf16 high part and a
+//                 bf16 remainder (two MFMAs), leaving a relative weight error
+//                 of about 2^-18 instead of 2^-9.
 // Each sequence's query tokens are the last q_len positions of its context:
 // query token i sees keys j <= L - q_len + i (bottom-right causal alignment,
 // so a chunk attends to its cached prefix in full).  The grid is static:
@@ -40,8 +42,10 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;   // Q-block rows per workgroup
 constexpr int kKvTile = 32;          // keys per inner step
-constexpr int kLdsStride = kHeadDim + 8;  // K: bf16 elements per LDS row (272 B)
-constexpr int kVtStride = kKvTile + 4;    // V^T: bf16 elements per LDS row (72 B)
+constexpr int kLdsStride = kHeadDim + 8;   // K: bf16 elements per LDS row (272 B)
+constexpr int kVStride = kHeadDim + 48;    // V: bf16 elements per LDS row (352 B): the
+                                           // four rows of a transposing read group
+                                           // fall on disjoint banks
 constexpr int kBufs = 3;                  // LDS tile buffers
 constexpr int kPageCache = 2048;          // block-table entries staged in LDS (32k keys)
 constexpr float kLazyThreshold = 8.0f;
@@ -95,7 +99,7 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool 
 
 // LDS bytes prefill_body needs from its caller (K tiles, V^T tiles, page ids).
 constexpr int kPrefillSmemBytes =
-    kBufs * kKvTile * kLdsStride * 2 + kBufs * kHeadDim * kVtStride * 2 + kPageCache * 4;
+    kBufs * kKvTile * kLdsStride * 2 + kBufs * kKvTile * kVStride * 2 + kPageCache * 4;
 
 // One workgroup of kThreads threads: query tile / split / KV head number `id`
 // of the 1-D prefill grid (nx tiles x tile_splits x Hkv).  smem:
@@ -156,61 +160,55 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       qb[ks] = row_valid ? as_bf16x8(ld16(qrow + 16 * ks)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
-  // LDS, three buffers: K row-major [key][dim] (272-byte rows), V transposed
-  // [dim][key] (72-byte rows: 32 keys + pad), so both MFMA operands are plain
-  // 16- and 8-byte LDS reads.  While tile j is being finished (softmax, P.V),
-  // the S^T MFMAs of tile j+1 already run and tile j+2 is being stored: one
-  // barrier per tile.
+  // LDS, three buffers each of K and V, both row-major [key][dim] (padded
+  // rows).  While tile j is being finished (softmax, P.V), the S^T MFMAs of
+  // tile j+1 already run and tile j+2 is being stored: one barrier per tile.
   auto k_lds = reinterpret_cast<uint16_t(*)[kKvTile * kLdsStride]>(smem);
-  auto vt_lds = reinterpret_cast<uint16_t(*)[D * kVtStride]>(smem + kBufs * kKvTile * kLdsStride * 2);
+  auto v_lds =
+      reinterpret_cast<uint16_t(*)[kKvTile * kVStride]>(smem + kBufs * kKvTile * kLdsStride * 2);
 
-  // Tile loader: threads 0..255 stage K, threads 256..511 stage V; thread t
-  // (mod 256) handles keys 2*(t%16), 2*(t%16)+1 (same page) and dims
-  // 8*((t%256)/16) .. +7.  Loads are unconditional (a key past the context
-  // reads a valid page and its V row is zeroed when stored), so no load sits
-  // under a branch and the compiler keeps them in flight across the loop.
+  // Tile loader: thread t stages 16 bytes of K and 16 bytes of V of key
+  // t / 16, dims 8*(t%16) .. +7 (a wavefront moves four whole 256-byte rows
+  // of each), so every wavefront does the same staging work.  Loads are
+  // unconditional (a key past the context reads a valid page and its V row
+  // is zeroed when stored), so no load sits under a branch and the compiler
+  // keeps them in flight across the loop.
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
-  const bool v_side = tid >= 256;
-  const uint16_t* src = (v_side ? p.v_pool : p.k_pool) + (int64_t)g * p.stride_head;
-  const int kp = tid & 15, dc = (tid & 255) >> 4;
+  const int lkey = tid >> 4, ldc = tid & 15;
+  const int64_t loff = (int64_t)g * p.stride_head + (int64_t)(lkey % kPage) * p.stride_token + 8 * ldc;
+  const char* kth = reinterpret_cast<const char*>(p.k_pool + loff);
+  const char* vth = reinterpret_cast<const char*>(p.v_pool + loff);
+  const uint32_t page_bytes = (uint32_t)(p.stride_page * 2);  // < 2^32 (checked on the host)
   // Page ids of the current window of key tiles, staged in LDS, keep the
   // block-table lookup off each tile's load path.  Entries past the
   // context hold page 0 (never used: those keys are masked and zeroed).
   int* pg_lds = reinterpret_cast<int*>(smem + kBufs * kKvTile * kLdsStride * 2 +
-                                       kBufs * D * kVtStride * 2);
+                                       kBufs * kKvTile * kVStride * 2);
   constexpr int kWinTiles = kPageCache * kPage / kKvTile;
   const int nblk = (L + kPage - 1) / kPage;  // valid block-table entries
   int win0 = 0;                              // first key tile of the window
-  // tile t of the window -> two 16-byte loads into r
+  // tile t of the window -> r[0] = K, r[1] = V
   auto load_tile = [&](int t, uint4 (&r)[2]) {
-    const int key = (win0 + t) * kKvTile + 2 * kp;
-    const int64_t page = pg_lds[(win0 + t) * (kKvTile / kPage) + (2 * kp) / kPage -
-                                win0 * (kKvTile / kPage)];
-    const int64_t off = page * p.stride_page + (int64_t)(key % kPage) * p.stride_token + 8 * dc;
-    r[0] = ld16(src + off);
-    r[1] = ld16(src + off + p.stride_token);
+    const uint64_t off =
+        (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + lkey / kPage] * page_bytes;
+    r[0] = *reinterpret_cast<const uint4*>(kth + off);
+    r[1] = *reinterpret_cast<const uint4*>(vth + off);
   };
   auto store_tile = [&](int t, int buf, const uint4 (&r)[2]) {
-    const int key = (win0 + t) * kKvTile + 2 * kp;
-    if (!v_side) {
-      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp) * kLdsStride + 8 * dc]) = r[0];
-      *reinterpret_cast<uint4*>(&k_lds[buf][(2 * kp + 1) * kLdsStride + 8 * dc]) = r[1];
-    } else {
-      // V rows past the context are zeroed: stale data (even NaN) must not
-      // reach O through a zero weight
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 va = key < L ? r[0] : z, vb = key + 1 < L ? r[1] : z;
-      const uint32_t a[4] = {va.x, va.y, va.z, va.w};
-      const uint32_t b[4] = {vb.x, vb.y, vb.z, vb.w};
-      uint32_t* vt = reinterpret_cast<uint32_t*>(&vt_lds[buf][0]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 8dc+2w and 8dc+2w+1: (key 2kp, key 2kp+1) pairs
-        vt[((8 * dc + 2 * w) * kVtStride + 2 * kp) / 2] = (a[w] & 0xffffu) | (b[w] << 16);
-        vt[((8 * dc + 2 * w + 1) * kVtStride + 2 * kp) / 2] = (a[w] >> 16) | (b[w] & 0xffff0000u);
-      }
-    }
+    *reinterpret_cast<uint4*>(&k_lds[buf][lkey * kLdsStride + 8 * ldc]) = r[0];
+    // V rows past the context are zeroed: stale data (even NaN) must not
+    // reach O through a zero weight
+    const bool tail = (win0 + t + 1) * kKvTile > L;  // uniform
+    const uint4 v = (tail && (win0 + t) * kKvTile + lkey >= L) ? make_uint4(0, 0, 0, 0) : r[1];
+    *reinterpret_cast<uint4*>(&v_lds[buf][lkey * kVStride + 8 * ldc]) = v;
   };
+  // Transposing V reads: lane (group gq = lane / 16, r = lane % 16) points
+  // at key 4*half + r/4 (+16kk, +8 for the second read), dims
+  // 16*(gq%2) + 4*(r%4) (+32mt); it receives dim 16*(gq%2) + r (+32mt) for
+  // keys +0..3, the A-operand layout that matches P's B-operand keys
+  // 16kk + 8*(j/4) + 4*half + j%4.
+  const int vr_off = (4 * half + (lane & 15) / 4) * kVStride + 16 * ((lane >> 4) & 1) +
+                     4 * (lane & 3);
   // S^T = K Q^T for the tile in buffer buf, D = 128 in 8 steps of 16.
   auto qk = [&](int buf, f32x16& st) {
 #pragma unroll
@@ -283,8 +281,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     }
     lsum += psum;
 
-    // O^T += V^T P^T: two k-steps of 16 keys, four 32-dim M tiles.
-    const uint16_t* vt = &vt_lds[buf][0];
+    // O^T += V^T P^T: two k-steps of 16 keys, four 32-dim M tiles.  The
+    // buffer's base address is made opaque, so each of the sixteen reads is
+    // that base plus a constant the instruction's offset field holds (left
+    // alone, the compiler keeps sixteen hoisted addresses in registers and
+    // rebuilds each one every tile).
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    lds_i16x4* vb = (lds_i16x4*)&v_lds[buf][vr_off];
+    asm volatile("" : "+v"(vb));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * kk], pk[4 * kk + 1],
@@ -295,10 +299,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
                                                     pl[4 * kk + 3]));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const uint16_t* row = vt + (32 * mt + n) * kVtStride + 16 * kk + 4 * half;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row);      // keys +0..3
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 8);  // keys +8..11
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        // element offsets / 4: one i16x4 is 4 bf16
+        lds_i16x4* at = vb + (16 * kk * kVStride + 32 * mt) / 4;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at + 8 * kVStride / 4);
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                               __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y));
         o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[mt], 0, 0, 0);
         if constexpr (PRECISE)
           o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbl, o[mt], 0, 0, 0);
