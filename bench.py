@@ -182,7 +182,13 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    total_ms, per = time_replays(torch, g, [g], steps, warmup)
+    # four steps per replay, back to back as a serving loop issues them
+    per_replay = 4
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
+        for _ in range(per_replay):
+            step()
+    total_ms, per = time_replays(torch, g_all, [g] * per_replay, steps, warmup)
     flops = prefill_flops(b)
     nbytes = prefill_bytes(b)
     avg_ms = sum(per) / len(per)
@@ -301,8 +307,8 @@ def main():
         },
     }
     if not args.no_prefill:
-        result["prefill"] = bench_prefill(torch, pa, workloads, dev, max(5, args.steps // 5),
-                                          min(args.warmup, 3))
+        result["prefill"] = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
+                                          max(8, args.warmup))
         note(f"prefill: {result['prefill']['value']} TFLOP/s")
     if args.all:
         others = {}
@@ -316,8 +322,8 @@ def main():
                             "num_splits": dd["tiles"].num_splits}
             note(f"{name}: {others[name]}")
             del dd
-        mixed = bench_prefill(torch, pa, workloads, dev, max(5, args.steps // 5),
-                              min(args.warmup, 3), name="mixed_unified")
+        mixed = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
+                              max(8, args.warmup), name="mixed_unified")
         others["mixed_unified"] = mixed
         note(f"mixed_unified: {mixed['ms_per_step'] * 1e3:.1f} us, {mixed['gb_per_s']} GB/s, "
              f"{mixed['value']} TFLOP/s, whole-launch frac {mixed['whole_launch_roofline_frac']}")
