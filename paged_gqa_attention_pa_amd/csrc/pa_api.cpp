@@ -140,31 +140,24 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
   const int G = problem->num_q_heads / problem->num_kv_heads;
   pa_tiles t;
   memset(&t, 0, sizeof t);
+  const pa::DecodeChoice dc = pa::table_decode(problem->num_seqs, problem->num_kv_heads,
+                                               problem->max_context_len, G);
   if (problem->max_query_len <= 1) {
     t.kv_tile = pa::kDecodeTile;
-    t.waves_per_wg = pa::table_decode_waves(problem->num_seqs, problem->num_kv_heads,
-                                            problem->max_context_len, G);
+    t.waves_per_wg = dc.waves;
     t.q_tokens_per_tile = 1;
-    t.num_splits = pa::table_decode_splits(problem->num_seqs, problem->num_kv_heads,
-                                           problem->max_context_len);
-    t.variant = pa::table_decode_variant(problem->num_seqs, problem->num_kv_heads,
-                                         problem->max_context_len);
+    t.num_splits = dc.splits;
+    t.variant = dc.variant;
   } else {
     t.kv_tile = 32;
     t.waves_per_wg = 8;
     t.q_tokens_per_tile = 256 / G;
     // single-token sequences of a mixed batch run as split-KV decode work
-    t.num_splits = may_hold_decode_rows(problem)
-                       ? pa::table_decode_splits(problem->num_seqs, problem->num_kv_heads,
-                                                 problem->max_context_len)
-                       : 1;
+    t.num_splits = may_hold_decode_rows(problem) ? dc.splits : 1;
     // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18;
     // single-token sequences take the decode table's grid choice
     t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
-                pa::kVariantSeparateMerge |
-                (pa::table_decode_variant(problem->num_seqs, problem->num_kv_heads,
-                                          problem->max_context_len) &
-                 pa::kVariantEvenWork);
+                pa::kVariantSeparateMerge | (dc.variant & pa::kVariantEvenWork);
     // Split query tiles only in batches without single-token sequences:
     // measured on gfx950, decode workgroups already use the CUs that a few
     // long query tiles leave idle, and splitting the tiles then only adds
@@ -172,10 +165,9 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     // 295 us with two runs per tile; the chunks alone: 197 us -> 134 us).
     t.tile_splits = may_hold_decode_rows(problem)
                         ? 1
-                        : pa::table_prefill_tile_splits(problem->total_query_tokens,
-                                                        t.q_tokens_per_tile,
-                                                        problem->num_kv_heads,
-                                                        problem->max_context_len);
+                        : pa::table_prefill_splits(problem->total_query_tokens,
+                                                   t.q_tokens_per_tile, problem->num_kv_heads,
+                                                   problem->max_context_len);
   }
   *out = t;
   return pa_workspace_size(problem, &t, workspace_bytes);

@@ -9,7 +9,11 @@
 
 #include <stdint.h>
 
+#include "pa_tile_table_gen.h"
+
 namespace pa {
+
+// Fallback rules below cover shapes outside the swept buckets.
 
 inline int table_decode_splits(int num_seqs, int num_kv_heads, int max_context_len) {
   const int64_t ntiles = (max_context_len + 15) / 16;
@@ -60,6 +64,51 @@ inline int table_prefill_tile_splits(int64_t prefill_tokens, int q_tile, int num
   if (s > s_keys) s = s_keys;
   if (s > 8) s = 8;
   return s < 1 ? 1 : (int)s;
+}
+
+// Index of the first bucket >= v, or -1 past the last one.
+template <int N>
+inline int bucket_of(const int (&buckets)[N], int64_t v) {
+  for (int i = 0; i < N; ++i)
+    if (v <= buckets[i]) return i;
+  return -1;
+}
+
+struct DecodeChoice {
+  int splits, waves, variant;
+};
+
+// Decode launch shape: the swept entry for (units, context-bound) bucket when
+// there is one, else the fallback rules.
+inline DecodeChoice table_decode(int num_seqs, int num_kv_heads, int max_context_len,
+                                 int group) {
+  DecodeChoice c{table_decode_splits(num_seqs, num_kv_heads, max_context_len),
+                 table_decode_waves(num_seqs, num_kv_heads, max_context_len, group),
+                 table_decode_variant(num_seqs, num_kv_heads, max_context_len)};
+  const int ui = bucket_of(gen::kUnitBuckets, (int64_t)num_seqs * num_kv_heads);
+  const int ci = bucket_of(gen::kCtxBuckets, max_context_len);
+  if (ui >= 0 && ci >= 0 && gen::kDecode[ui][ci][0] > 0) {
+    c.splits = gen::kDecode[ui][ci][0];
+    c.waves = gen::kDecode[ui][ci][1];
+    c.variant = gen::kDecode[ui][ci][2];
+  }
+  if (group >= 16) c.waves = 4;  // the only G = 16 build
+  if (c.splits <= 1) {
+    c.splits = 1;
+    c.variant = 2;
+  }
+  return c;
+}
+
+// Prefill tile_splits for a batch without single-token sequences.
+inline int table_prefill_splits(int64_t total_query_tokens, int q_tile, int num_kv_heads,
+                                 int max_context_len) {
+  const int64_t wgs = (total_query_tokens + q_tile - 1) / q_tile * num_kv_heads;
+  const int wi = bucket_of(gen::kPfWgBuckets, wgs);
+  const int ci = bucket_of(gen::kPfCtxBuckets, max_context_len);
+  if (wi >= 0 && ci >= 0 && gen::kPrefillTileSplits[wi][ci] > 0)
+    return gen::kPrefillTileSplits[wi][ci];
+  return table_prefill_tile_splits(total_query_tokens, q_tile, num_kv_heads, max_context_len);
 }
 
 }  // namespace pa

@@ -70,8 +70,8 @@ def test_select_tiles_decode_and_prefill(lib):
     T = 2 * 512
     st, t, ws = _select(lib, _problem(num_seqs=2, max_query_len=512, total_query_tokens=T,
                                       max_context_len=4608, max_blocks_per_seq=512))
-    assert st == pa.PA_OK and t.tile_splits == 2 and t.num_splits == 1
-    assert ws >= T * 32 * 2 * 129 * 4
+    assert st == pa.PA_OK and t.tile_splits > 1 and t.num_splits == 1
+    assert ws >= T * 32 * t.tile_splits * 129 * 4
     # the same chunks beside decode rows: decode splits, no tile split
     st, t, ws = _select(lib, _problem(num_seqs=18, max_query_len=512, total_query_tokens=T + 16,
                                       max_context_len=16384, max_blocks_per_seq=1024))
