@@ -36,9 +36,16 @@ DECODE_BYTES_PER_TOKEN = 4096
 # (scaled by a plain copy of known size), for the kernel as last profiled;
 # None until counters are taken for the current kernel.
 TRAFFIC = {
-    # decode_kernel<4,4,false> + splitkv_reduce_kernel, num_splits 32
+    # decode_kernel<4,8,false> + splitkv_reduce_kernel, num_splits 32
     # (profiles/decode_ctx32k_hbm_counters.md)
-    "decode_ctx32k": 135690857,
+    "decode_ctx32k": 135737957,
+}
+# The same for one pa_prefill call (unified kernel, + merges when present).
+PREFILL_TRAFFIC = {
+    # unified_kernel<4,false> (profiles/prefill_chunk2048_hbm_counters.md)
+    "prefill_chunk2048": 185374421,
+    # unified_kernel<4,false> + splitkv_reduce_kernel (profiles/mixed_unified_kernel_trace.md)
+    "mixed_unified": 643105086,
 }
 
 
@@ -57,6 +64,8 @@ def parse():
     ap.add_argument("--waves", type=int, default=0, help="force waves per workgroup (0 = table)")
     ap.add_argument("--variant", type=int, default=-1, help="force pa_tiles.variant (-1 = table)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-workload", default="prefill_chunk2048",
+                    help="workload of --prefill-only (prefill_chunk2048 or mixed_unified)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill workload (profiling runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -202,7 +211,8 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
             "tiles": tiles.as_dict(),
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None}}
+                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                         "traffic": PREFILL_TRAFFIC.get(name)}}
 
 
 def calibrate_copy(torch, dev, mib):
@@ -259,7 +269,8 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.prefill_only:
-        pre = bench_prefill(torch, pa, workloads, dev, args.steps, args.warmup)
+        pre = bench_prefill(torch, pa, workloads, dev, args.steps, args.warmup,
+                            name=args.prefill_workload)
         note(f"prefill: {pre['value']} TFLOP/s")
         calibrate_copy(torch, dev, args.calibrate_copy)
         print(json.dumps(pre), flush=True)

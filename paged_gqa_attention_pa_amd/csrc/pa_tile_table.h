@@ -74,6 +74,16 @@ inline int bucket_of(const int (&buckets)[N], int64_t v) {
   return -1;
 }
 
+// Index of the last bucket <= v (0 below the first).  Units round down: a
+// batch with fewer (sequence, kv head) units than a bucket wants at least
+// that bucket's split count, never fewer.
+template <int N>
+inline int bucket_floor(const int (&buckets)[N], int64_t v) {
+  int i = 0;
+  while (i + 1 < N && buckets[i + 1] <= v) ++i;
+  return i;
+}
+
 struct DecodeChoice {
   int splits, waves, variant;
 };
@@ -85,7 +95,10 @@ inline DecodeChoice table_decode(int num_seqs, int num_kv_heads, int max_context
   DecodeChoice c{table_decode_splits(num_seqs, num_kv_heads, max_context_len),
                  table_decode_waves(num_seqs, num_kv_heads, max_context_len, group),
                  table_decode_variant(num_seqs, num_kv_heads, max_context_len)};
-  const int ui = bucket_of(gen::kUnitBuckets, (int64_t)num_seqs * num_kv_heads);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int ui = units > 2 * gen::kUnitBuckets[sizeof(gen::kUnitBuckets) / sizeof(int) - 1]
+                     ? -1
+                     : bucket_floor(gen::kUnitBuckets, units);
   const int ci = bucket_of(gen::kCtxBuckets, max_context_len);
   if (ui >= 0 && ci >= 0 && gen::kDecode[ui][ci][0] > 0) {
     c.splits = gen::kDecode[ui][ci][0];
