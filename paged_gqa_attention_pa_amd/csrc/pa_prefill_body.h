@@ -46,7 +46,8 @@ constexpr int kLdsStride = kHeadDim + 8;   // K: bf16 elements per LDS row (272 
 constexpr int kVStride = kHeadDim + 48;    // V: bf16 elements per LDS row (352 B): the
                                            // four rows of a transposing read group
                                            // fall on disjoint banks
-constexpr int kBufs = 3;                  // LDS tile buffers
+constexpr int kKBufs = 4;                 // LDS K tile buffers
+constexpr int kVBufs = 5;                 // LDS V tile buffers (V is read one step later)
 constexpr int kPageCache = 2048;          // block-table entries staged in LDS (32k keys)
 constexpr float kLazyThreshold = 8.0f;
 
@@ -99,7 +100,7 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool 
 
 // LDS bytes prefill_body needs from its caller (K tiles, V^T tiles, page ids).
 constexpr int kPrefillSmemBytes =
-    kBufs * kKvTile * kLdsStride * 2 + kBufs * kKvTile * kVStride * 2 + kPageCache * 4;
+    kKBufs * kKvTile * kLdsStride * 2 + kVBufs * kKvTile * kVStride * 2 + kPageCache * 4;
 
 // One workgroup of kThreads threads: query tile / split / KV head number `id`
 // of the 1-D prefill grid (nx tiles x tile_splits x Hkv).  smem:
@@ -165,7 +166,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // tile j+1 already run and tile j+2 is being stored: one barrier per tile.
   auto k_lds = reinterpret_cast<uint16_t(*)[kKvTile * kLdsStride]>(smem);
   auto v_lds =
-      reinterpret_cast<uint16_t(*)[kKvTile * kVStride]>(smem + kBufs * kKvTile * kLdsStride * 2);
+      reinterpret_cast<uint16_t(*)[kKvTile * kVStride]>(smem + kKBufs * kKvTile * kLdsStride * 2);
 
   // Tile loader: thread t stages 16 bytes of K and 16 bytes of V of key
   // t / 16, dims 8*(t%16) .. +7 (a wavefront moves four whole 256-byte rows
@@ -182,8 +183,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // Page ids of the current window of key tiles, staged in LDS, keep the
   // block-table lookup off each tile's load path.  Entries past the
   // context hold page 0 (never used: those keys are masked and zeroed).
-  int* pg_lds = reinterpret_cast<int*>(smem + kBufs * kKvTile * kLdsStride * 2 +
-                                       kBufs * kKvTile * kVStride * 2);
+  int* pg_lds = reinterpret_cast<int*>(smem + kKBufs * kKvTile * kLdsStride * 2 +
+                                       kVBufs * kKvTile * kVStride * 2);
   constexpr int kWinTiles = kPageCache * kPage / kKvTile;
   const int nblk = (L + kPage - 1) / kPage;  // valid block-table entries
   int win0 = 0;                              // first key tile of the window
@@ -194,13 +195,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     r[0] = *reinterpret_cast<const uint4*>(kth + off);
     r[1] = *reinterpret_cast<const uint4*>(vth + off);
   };
-  auto store_tile = [&](int t, int buf, const uint4 (&r)[2]) {
-    *reinterpret_cast<uint4*>(&k_lds[buf][lkey * kLdsStride + 8 * ldc]) = r[0];
+  auto store_tile = [&](int t, int kbuf, int vbuf, const uint4 (&r)[2]) {
+    *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) = r[0];
     // V rows past the context are zeroed: stale data (even NaN) must not
     // reach O through a zero weight
     const bool tail = (win0 + t + 1) * kKvTile > L;  // uniform
     const uint4 v = (tail && (win0 + t) * kKvTile + lkey >= L) ? make_uint4(0, 0, 0, 0) : r[1];
-    *reinterpret_cast<uint4*>(&v_lds[buf][lkey * kVStride + 8 * ldc]) = v;
+    *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) = v;
   };
   // Transposing V reads: lane (group gq = lane / 16, r = lane % 16) points
   // at key 4*half + r/4 (+16kk, +8 for the second read), dims
@@ -209,19 +210,26 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // 16kk + 8*(j/4) + 4*half + j%4.
   const int vr_off = (4 * half + (lane & 15) / 4) * kVStride + 16 * ((lane >> 4) & 1) +
                      4 * (lane & 3);
-  // S^T = K Q^T for the tile in buffer buf, D = 128 in 8 steps of 16.
+  // S^T = K Q^T for the tile in buffer buf, D = 128 in 8 steps of 16.  All
+  // eight K operands are read before the first MFMA (the scheduling barrier
+  // keeps the compiler from sinking each read next to its MFMA, which would
+  // put an LDS round trip between every pair of dependent MFMAs).
   auto qk = [&](int buf, f32x16& st) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st[e] = 0.f;
+    bf16x8 ka[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       // two 8-byte LDS reads: measured faster than one 16-byte read on gfx950
       const uint16_t* kr = &k_lds[buf][n * kLdsStride + 16 * ks + 8 * half];
       const uint2 a0 = *reinterpret_cast<const uint2*>(kr);
       const uint2 a1 = *reinterpret_cast<const uint2*>(kr + 4);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)), qb[ks], st, 0, 0, 0);
+      ka[ks] = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], st, 0, 0, 0);
   };
 
   f32x16 o[4];
@@ -233,9 +241,11 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   const float c = p.scale_log2;  // > 0 (checked on the host)
   f32x16 st_cur, st_next;
 
-  // One key tile: softmax of tile jg (its S^T in st_cur, its V^T in buffer
-  // buf) and O^T += V^T P^T.
-  auto softmax_pv = [&](int jg, int buf) {
+  // Softmax of key tile jg (its S^T in st_cur): P rounded to bf16 in pk
+  // (and its bf16 remainder in pl for the precise variant), the running max
+  // and sum updated, O rescaled when the max rises.
+  uint32_t pk[8], pl[8];
+  auto softmax = [&](int jg) {
     // Register e holds key 8*(e/4) + 4*half + e%4 of the tile, row n; the
     // log2-domain logit is c*S (c > 0, so the max can be taken on S).
     const bool full = jg * kKvTile + kKvTile <= wave_limit;  // no key of the tile masked
@@ -264,7 +274,6 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
         for (int e = 0; e < 16; ++e) o[mt][e] *= alpha;
     }
     const float neg_m = (m == kNegInf) ? 0.f : -m;
-    uint32_t pk[8], pl[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
@@ -280,14 +289,17 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       }
     }
     lsum += psum;
+  };
 
-    // O^T += V^T P^T: two k-steps of 16 keys, four 32-dim M tiles.  The
-    // buffer's base address is made opaque, so each of the sixteen reads is
-    // that base plus a constant the instruction's offset field holds (left
-    // alone, the compiler keeps sixteen hoisted addresses in registers and
-    // rebuilds each one every tile).
+  // O^T += V^T P^T for the tile whose V is in buffer vbuf and whose P is in
+  // pk / pl: two k-steps of 16 keys, four 32-dim M tiles.  The buffer's base
+  // address is made opaque, so each of the sixteen reads is that base plus a
+  // constant the instruction's offset field holds (left alone, the compiler
+  // keeps sixteen hoisted addresses in registers and rebuilds each one every
+  // tile).
+  auto pv = [&](int vbuf) {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    lds_i16x4* vb = (lds_i16x4*)&v_lds[buf][vr_off];
+    lds_i16x4* vb = (lds_i16x4*)&v_lds[vbuf][vr_off];
     asm volatile("" : "+v"(vb));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -297,28 +309,44 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       if constexpr (PRECISE)
         pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2],
                                                     pl[4 * kk + 3]));
+      bf16x8 va[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         // element offsets / 4: one i16x4 is 4 bf16
         lds_i16x4* at = vb + (16 * kk * kVStride + 32 * mt) / 4;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at + 8 * kVStride / 4);
-        const bf16x8 va = __builtin_bit_cast(
+        va[mt] = __builtin_bit_cast(
             bf16x8, make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
                                __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y));
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pb, o[mt], 0, 0, 0);
         if constexpr (PRECISE)
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbl, o[mt], 0, 0, 0);
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pbl, o[mt], 0, 0, 0);
       }
     }
   };
 
   // The run [j0, j0 + nkv) in windows of at most kWinTiles key tiles (one
-  // LDS page-id window each).  Inside a window, three LDS buffers: while tile
-  // j is finished (softmax, P.V), the S^T MFMAs of tile j+1 already run,
-  // tile j+2 is stored from registers and tile j+3's global loads are in
-  // flight (two register sets, so a tile's loads have two iterations to
-  // land); one barrier per tile.
+  // LDS page-id window each).  Each step j is two phases, each ending in a
+  // workgroup barrier:
+  //   M(j): S^T of tile j+1 and P.V of tile j-1 (sixteen MFMAs);
+  //   V(j): softmax of tile j, store of tile j+3 (loaded during V(j-1)),
+  //         loads of tile j+4.
+  // Wavefronts 4..7 run one phase behind wavefronts 0..3 (one extra barrier
+  // at the start of a window for them, at its end for the others), and each
+  // SIMD holds one wavefront of each group, so while one of its wavefronts
+  // issues MFMAs the other computes exponentials.  K of tile t is read in
+  // M(t-1) of both groups, V of tile t in M(t+1): four K buffers and five V
+  // buffers keep every store clear of reads still pending in the lagging
+  // group.
+  // wavefront-uniform, and visibly so to the compiler (readfirstlane), so
+  // the extra barriers below sit behind scalar branches: a wavefront that
+  // does not take them never executes them
+  const bool lag = __builtin_amdgcn_readfirstlane(wave) >= kWaves / 2;
   for (int wbeg = 0; wbeg < nkv; wbeg += kWinTiles) {
     const int nw = min(kWinTiles, nkv - wbeg);
     win0 = j0 + wbeg;
@@ -328,29 +356,31 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       for (int i = tid; i < nb; i += kThreads) pg_lds[i] = (b0 + i < nblk) ? bt[b0 + i] : 0;
       __syncthreads();
     }
-    uint4 ra[2], rb[2];
-    load_tile(0, ra);
-    load_tile(min(1, nw - 1), rb);
-    store_tile(0, 0, ra);
-    if (nw > 1) store_tile(1, 1, rb);
-    __syncthreads();
-    load_tile(min(2, nw - 1), ra);
-    qk(0, st_cur);
-    // iteration j: ra/rb alternate as "tile j+2 (loaded)" / "tile j+3 (loading)"
-    auto step = [&](int j, uint4 (&cur)[2], uint4 (&nxt)[2]) {
-      if (j + 1 < nw) qk((j + 1) % kBufs, st_next);  // MFMA pipe, overlaps the softmax below
-      load_tile(min(j + 3, nw - 1), nxt);
-      softmax_pv(win0 + j, j % kBufs);
-      // tile j+2 goes to the buffer tile j-1 used (its last reads were before
-      // the previous barrier)
-      if (j + 2 < nw) store_tile(j + 2, (j + 2) % kBufs, cur);
-      __syncthreads();
-      st_cur = st_next;
-    };
-    for (int j = 0; j < nw; j += 2) {
-      step(j, ra, rb);
-      if (j + 1 < nw) step(j + 1, rb, ra);
+    uint4 rg[2];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      load_tile(min(t, nw - 1), rg);
+      if (t < nw) store_tile(t, t, t, rg);
     }
+    load_tile(min(3, nw - 1), rg);
+    __syncthreads();
+    qk(0, st_cur);
+    if (lag) __syncthreads();
+    for (int j = 0; j < nw; ++j) {
+      // M(j)
+      if (j + 1 < nw) qk((j + 1) % kKBufs, st_next);
+      if (j >= 1) pv((j - 1) % kVBufs);
+      __syncthreads();
+      // V(j)
+      softmax(win0 + j);
+      if (j + 3 < nw) store_tile(j + 3, (j + 3) % kKBufs, (j + 3) % kVBufs, rg);
+      load_tile(min(j + 4, nw - 1), rg);
+      st_cur = st_next;
+      __syncthreads();
+    }
+    pv((nw - 1) % kVBufs);  // M(nw): P.V of the last tile
+    __syncthreads();
+    if (!lag) __syncthreads();
   }
 
   const f32x2 lh = halves(lsum);
