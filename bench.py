@@ -73,6 +73,9 @@ def parse():
                          "kernel for scaling HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--launch-study", action="store_true",
+                    help="time one decode step eagerly, as one graph replay, and as one of "
+                         "eight steps in a replay, per decode workload; print one JSON line")
     ap.add_argument("--all", action="store_true",
                     help="also time the other workloads (decode_ctx512, decode_b64, "
                          "mixed_unified) and report them under 'others'")
@@ -215,6 +218,56 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
                          "traffic": PREFILL_TRAFFIC.get(name)}}
 
 
+def launch_study(torch, pa, workloads, dev, reps=40):
+    """Launch overhead of a decode step on this chip: the same pa_decode call
+    issued eagerly from Python (two kernel launches through the C ABI), as a
+    one-step graph replay, and inside an eight-step graph replay.  The pools
+    are not rotated, so short contexts are served from the caches: this
+    isolates launch cost, not bandwidth."""
+    out = {}
+    for name in ("decode_ctx512", "decode_ctx32k", "decode_b64"):
+        spec = workloads.WORKLOADS[name]
+        b = workloads.generate(spec, dev, fill="zero")
+        max_ctx = b.max_context_len
+        pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale, max_ctx, 1)
+        tiles, ws = pa.select_tiles(pb)
+        workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        o = torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)
+
+        def step():
+            pa.decode(b.q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, spec.scale,
+                      max_ctx, out=o, tiles=tiles, workspace=workspace, problem=pb)
+
+        def timed(fn, n_per):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * n_per)
+
+        eager = timed(step, 1)
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            step()
+        g8 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g8):
+            for _ in range(8):
+                step()
+        out[name] = {"eager_us": round(eager, 2), "graph_1_us": round(timed(g1.replay, 1), 2),
+                     "graph_8_us": round(timed(g8.replay, 8), 2),
+                     "kernels_per_step": 2 if tiles.num_splits > 1 else 1}
+        note(f"{name}: {out[name]}")
+        del b, g1, g8
+        torch.cuda.empty_cache()
+    return out
+
+
 def calibrate_copy(torch, dev, mib):
     """Plain device-to-device copies of a known size (for counter scaling)."""
     if mib <= 0:
@@ -268,6 +321,9 @@ def main():
     pa.load()
     dev = torch.device("cuda:0")
 
+    if args.launch_study:
+        print(json.dumps({"launch_study": launch_study(torch, pa, workloads, dev)}), flush=True)
+        return
     if args.prefill_only:
         pre = bench_prefill(torch, pa, workloads, dev, args.steps, args.warmup,
                             name=args.prefill_workload)
