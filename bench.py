@@ -48,6 +48,9 @@ PREFILL_TRAFFIC = {
     "mixed_unified": 643105086,
 }
 
+# The same for one pa_cache_append call (append_kernel).
+APPEND_TRAFFIC = {}
+
 
 def note(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -66,6 +69,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-workload", default="prefill_chunk2048",
                     help="workload of --prefill-only (prefill_chunk2048 or mixed_unified)")
+    ap.add_argument("--append-only", action="store_true",
+                    help="time only pa_cache_append on --prefill-workload (for profiling)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill workload (profiling runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -218,6 +223,58 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
                          "traffic": PREFILL_TRAFFIC.get(name)}}
 
 
+def append_bytes(b):
+    """Algorithmic bytes of a paged KV append: each new token's K and V rows
+    (Hkv * D bf16 each) read once and written once."""
+    return b.num_tokens * b.spec.num_kv_heads * b.spec.head_dim * 2 * 2 * 2
+
+
+def bench_append(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2048",
+                 copies=8):
+    """pa_cache_append of a batch's new tokens.  Each step appends a different
+    copy of the new rows into a different copy of the pools (copies of both
+    together exceed the 256 MiB Infinity Cache for the chunked prefill), so
+    the rows stream from HBM and the written pages leave for HBM."""
+    spec = workloads.WORKLOADS[name]
+    b = workloads.generate(spec, dev, fill="zero")
+    sets = []
+    for i in range(copies):
+        kn, vn = workloads.new_kv(b, seed=500 + i)
+        kp, vp = (b.k_pool, b.v_pool) if i == 0 else (b.k_pool.clone(), b.v_pool.clone())
+        sets.append((kn, vn, kp, vp))
+    problem = pa.make_problem(sets[0][0], b.k_pool, b.block_tables, b.num_seqs, 1.0, 0, 1)
+
+    def step(kn, vn, kp, vp):
+        pa.cache_append(kn, vn, kp, vp, b.block_tables, b.context_lens, b.query_start_loc,
+                        problem=problem)
+
+    for st in sets:
+        step(*st)
+    torch.cuda.synchronize()
+    singles = []
+    for st in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(*st)
+        singles.append(g)
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
+        for st in sets:
+            step(*st)
+    total_ms, per = time_replays(torch, g_all, singles, steps, warmup)
+    avg_ms = sum(per) / len(per)
+    nbytes = append_bytes(b)
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"workload": f"{name}: append {b.num_tokens} new tokens x {spec.num_kv_heads} kv "
+                        f"heads (K and V) into their pages",
+            "metric": "paged KV append GB/s (new rows read + written)",
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(avg_ms * 1e3, 2),
+            "bytes_per_step": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": APPEND_TRAFFIC.get(name)}}
+
+
 def launch_study(torch, pa, workloads, dev, reps=40):
     """Launch overhead of a decode step on this chip: the same pa_decode call
     issued eagerly from Python (two kernel launches through the C ABI), as a
@@ -324,6 +381,12 @@ def main():
     if args.launch_study:
         print(json.dumps({"launch_study": launch_study(torch, pa, workloads, dev)}), flush=True)
         return
+    if args.append_only:
+        app = bench_append(torch, pa, workloads, dev, args.steps, args.warmup,
+                           name=args.prefill_workload)
+        note(f"append: {app['us_per_step']} us, {app['value']} GB/s")
+        print(json.dumps(app), flush=True)
+        return
     if args.prefill_only:
         pre = bench_prefill(torch, pa, workloads, dev, args.steps, args.warmup,
                             name=args.prefill_workload)
@@ -377,6 +440,10 @@ def main():
         result["prefill"] = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
                                           max(8, args.warmup))
         note(f"prefill: {result['prefill']['value']} TFLOP/s")
+    if not args.no_prefill:
+        result["append"] = bench_append(torch, pa, workloads, dev, max(16, args.steps // 2),
+                                        max(8, args.warmup))
+        note(f"append: {result['append']['us_per_step']} us, {result['append']['value']} GB/s")
     if args.all:
         others = {}
         for name in ("decode_ctx512", "decode_b64"):
@@ -392,6 +459,10 @@ def main():
         mixed = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
                               max(8, args.warmup), name="mixed_unified")
         others["mixed_unified"] = mixed
+        app = bench_append(torch, pa, workloads, dev, max(16, args.steps // 2),
+                           max(8, args.warmup), name="decode_b64", copies=2)
+        others["append_decode_b64"] = app
+        note(f"append decode_b64: {app['us_per_step']} us")
         note(f"mixed_unified: {mixed['ms_per_step'] * 1e3:.1f} us, {mixed['gb_per_s']} GB/s, "
              f"{mixed['value']} TFLOP/s, whole-launch frac {mixed['whole_launch_roofline_frac']}")
         result["others"] = others

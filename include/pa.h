@@ -191,6 +191,27 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
                             int32_t num_splits, int32_t head_dim, void* out,
                             pa_dtype out_dtype, float* lse_out, hipStream_t stream);
 
+/* Paged KV append: the step just before attention that writes the new
+ * tokens' K and V into their block-table slots, so a chunk attends to its
+ * prefix and to itself from the pages ([IBM-PA] model-feature list: paged KV
+ * cache with prefix caching; the cache layout is that of pa_prefill).
+ * Token i of sequence s (0 <= i < q_len(s)) goes to logical position
+ * p = context_lens[s] - q_len(s) + i, i.e. page block_tables[s][p / P],
+ * slot p % P, kv head h, at page*kv_stride_page + slot*kv_stride_token +
+ * h*kv_stride_head; context_lens counts the new tokens, as for pa_prefill.
+ * k_new, v_new: bf16 [T, Hkv, D] (row t = one token, D contiguous), rows in
+ * query_start_loc order; query_start_loc NULL means one token per sequence
+ * (T = num_seqs, decode).  T = problem->total_query_tokens.  k_pool,
+ * v_pool: the caller's paged pools, written only at those slots.  Every
+ * block-table entry a token lands in must be a valid page; a sequence with
+ * context_lens[s] < q_len(s) is undefined (its tokens are skipped).
+ * Pointers to bf16 data must be 16-byte aligned.  Host checks as for the
+ * other calls; nothing is allocated. */
+pa_status pa_cache_append(const pa_problem* problem, const void* k_new, const void* v_new,
+                          const int32_t* query_start_loc, const int32_t* block_tables,
+                          const int32_t* context_lens, void* k_pool, void* v_pool,
+                          hipStream_t stream);
+
 /* Static text for a status code. */
 const char* pa_status_string(pa_status status);
 

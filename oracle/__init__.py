@@ -48,6 +48,9 @@ class Oracle:
         lib.pa_oracle_partials.restype = ctypes.c_int
         lib.pa_oracle_merge.argtypes = [P, P, i64, i32, i32, P, P]
         lib.pa_oracle_merge.restype = ctypes.c_int
+        lib.pa_oracle_append.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i64, i64, i64, i64,
+                                         P, i32, P]
+        lib.pa_oracle_append.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
 
@@ -59,6 +62,11 @@ class Oracle:
 
     def merge(self, partial_o, partial_lse):
         return _merge(self.lib, partial_o, partial_lse)
+
+    def append(self, k_pool, v_pool, page_size, strides, k_new, v_new, block_tables,
+               context_lens, query_start_loc=None):
+        return _append(self.lib, k_pool, v_pool, page_size, strides, k_new, v_new,
+                       block_tables, context_lens, query_start_loc)
 
 
 def default() -> Oracle:
@@ -169,6 +177,34 @@ def _merge(lib, partial_o, partial_lse):
     return out, lse
 
 
+def _append(lib, k_pool, v_pool, page_size, strides, k_new, v_new, block_tables,
+            context_lens, query_start_loc=None):
+    kp = np.array(k_pool, dtype=np.uint16, copy=True, order="C")
+    vp = np.array(v_pool, dtype=np.uint16, copy=True, order="C")
+    if kp.shape != vp.shape:
+        raise ValueError("K and V pools must have one shape")
+    kn = np.ascontiguousarray(k_new, dtype=np.uint16)
+    vn = np.ascontiguousarray(v_new, dtype=np.uint16)
+    if kn.ndim != 3 or kn.shape != vn.shape:
+        raise ValueError("k_new and v_new must be [T, Hkv, D] of one shape")
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qsl = None if query_start_loc is None else np.ascontiguousarray(query_start_loc,
+                                                                    dtype=np.int32)
+    B = int(cl.shape[0])
+    T = B if qsl is None else int(qsl[-1])
+    if kn.shape[0] != T:
+        raise ValueError("k_new rows must match the new tokens")
+    rc = lib.pa_oracle_append(B, int(kn.shape[1]), int(kn.shape[2]), int(page_size),
+                              _ptr(kn), _ptr(vn),
+                              _ptr(qsl), _ptr(kp), _ptr(vp), int(kp.size), int(strides[0]),
+                              int(strides[1]), int(strides[2]), _ptr(bt), int(bt.shape[1]),
+                              _ptr(cl))
+    if rc != 0:
+        raise RuntimeError(f"pa_oracle_append failed ({rc})")
+    return kp, vp
+
+
 def attention(inp: PagedInputs, rows=None, threads: Optional[int] = None):
     """Single-pass attention.  rows: flat indices token*Hq + head, or None for
     every (token, head).  Returns (out fp64 [n, D], lse fp64 [n])."""
@@ -185,3 +221,12 @@ def partials(inp: PagedInputs, split_tokens: int, num_splits: int, rows=None,
 def merge(partial_o, partial_lse):
     """Log-sum-exp merge of [rows, S, D] partials.  Returns (O [rows, D], LSE [rows])."""
     return default().merge(partial_o, partial_lse)
+
+
+def append(k_pool, v_pool, page_size, strides, k_new, v_new, block_tables, context_lens,
+           query_start_loc=None):
+    """Paged KV append on copies of the pools (uint16 bf16 bits, any shape;
+    element (page, slot, head, d) at the given (page, token, head) strides,
+    d stride 1).  Returns the written copies (k_pool, v_pool)."""
+    return default().append(k_pool, v_pool, page_size, strides, k_new, v_new, block_tables,
+                            context_lens, query_start_loc)

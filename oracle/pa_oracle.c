@@ -32,6 +32,12 @@
  *     lse_k = m_k + ln l_k; with M = max_k lse_k and w_k = exp(lse_k - M),
  *     O = sum_k w_k O_k / sum_k w_k and LSE = M + ln sum_k w_k.
  *
+ *   - Paged KV append, the write that precedes attention: the q_s new tokens
+ *     of a sequence are the last q_s positions of its L_s-token context
+ *     (same reading as the causal rule), so new token i lands at position
+ *     L_s - q_s + i, in the page the block table names for that position,
+ *     at slot position mod P ([IBM-PA] model-feature list: paged KV cache).
+ *
  * The softmax here is the plain two-pass one (max, then exponentials and
  * sums), in fp64, over logical token positions in order.  bf16 inputs are
  * widened to fp64 exactly.  Nothing is tiled, fused or reordered.
@@ -266,6 +272,48 @@ int pa_oracle_merge(const double *partial_o, const double *partial_lse, int64_t 
     }
     for (int32_t d = 0; d < head_dim; ++d) o[d] /= wsum;
     lse[r] = M + log(wsum);
+  }
+  return 0;
+}
+
+/* Paged KV append: copy the K and V rows of every new token into its slot.
+ * k_new, v_new are [T, Hkv, D] bf16 bits, T = query_start_loc[num_seqs]
+ * (or num_seqs when query_start_loc is NULL: one token per sequence).
+ * For sequence s with q_s new tokens and L_s = context_lens[s], token i
+ * (row query_start_loc[s] + i) is logical position L_s - q_s + i; its row
+ * for kv head h goes to page BT[s][pos / P], slot pos mod P.  Sequences with
+ * L_s < q_s write nothing.  pool_elems bounds every write: a position past
+ * the table row or an offset past the pool returns -3 (pools may then be
+ * partly written).  Returns 0 on success. */
+int pa_oracle_append(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, const uint16_t *k_new, const uint16_t *v_new,
+                     const int32_t *query_start_loc, uint16_t *k_pool, uint16_t *v_pool,
+                     int64_t pool_elems, int64_t stride_page, int64_t stride_token,
+                     int64_t stride_head, const int32_t *block_tables, int32_t max_blocks,
+                     const int32_t *context_lens) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 || max_blocks <= 0)
+    return -2;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    int64_t first = query_start_loc ? query_start_loc[s] : s;
+    int64_t q_s = query_start_loc ? (int64_t)query_start_loc[s + 1] - first : 1;
+    int64_t L = context_lens[s];
+    if (L < q_s) continue;
+    for (int64_t i = 0; i < q_s; ++i) {
+      int64_t pos = L - q_s + i;
+      int64_t block = pos / page_size;
+      if (block >= max_blocks) return -3;
+      int64_t page = block_tables[(int64_t)s * max_blocks + block];
+      int64_t slot = pos % page_size;
+      for (int32_t h = 0; h < num_kv_heads; ++h) {
+        int64_t dst = page * stride_page + slot * stride_token + (int64_t)h * stride_head;
+        int64_t src = ((first + i) * num_kv_heads + h) * (int64_t)head_dim;
+        if (page < 0 || dst < 0 || dst + head_dim > pool_elems) return -3;
+        for (int32_t d = 0; d < head_dim; ++d) {
+          k_pool[dst + d] = k_new[src + d];
+          v_pool[dst + d] = v_new[src + d];
+        }
+      }
+    }
   }
   return 0;
 }

@@ -400,6 +400,37 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   return st;
 }
 
+pa_status pa_cache_append(const pa_problem* problem, const void* k_new, const void* v_new,
+                          const int32_t* query_start_loc, const int32_t* block_tables,
+                          const int32_t* context_lens, void* k_pool, void* v_pool,
+                          hipStream_t stream) {
+  pa_status st = check_problem(problem);
+  if (st != PA_OK) return st;
+  if (!k_new || !v_new || !block_tables || !context_lens || !k_pool || !v_pool)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_ERR_INVALID_ARG;
+  if (!query_start_loc && problem->total_query_tokens != problem->num_seqs)
+    return PA_ERR_INVALID_ARG;  // one token per sequence
+  if (problem->num_seqs == 0 || problem->total_query_tokens == 0) return PA_OK;
+  pa::AppendParams p;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.query_start_loc = query_start_loc;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.k_pool = static_cast<uint16_t*>(k_pool);
+  p.v_pool = static_cast<uint16_t*>(v_pool);
+  p.stride_page = problem->kv_stride_page;
+  p.stride_token = problem->kv_stride_token;
+  p.stride_head = problem->kv_stride_head;
+  p.num_seqs = problem->num_seqs;
+  p.num_kv_heads = problem->num_kv_heads;
+  p.max_blocks = problem->max_blocks_per_seq;
+  p.total_tokens = problem->total_query_tokens;
+  return from_hip(pa::launch_append(p, stream));
+}
+
 pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, int32_t rows,
                             int32_t num_splits, int32_t head_dim, void* out,
                             pa_dtype out_dtype, float* lse_out, hipStream_t stream) {

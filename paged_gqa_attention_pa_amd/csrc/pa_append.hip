@@ -1,0 +1,64 @@
+// Paged KV append for gfx950: new tokens' K and V rows into their pages.
+//
+// Token i of sequence s lands at logical position p = L_s - q_s + i (the
+// newest q_s positions of the context, the positions pa_prefill's queries
+// hold): page block_tables[s][p / P], slot p % P.  Sixteen threads move one
+// (token, kv head) row of 256 bytes for K and for V, 16 bytes each, so a
+// wavefront reads four whole rows of the token-major input and writes four
+// whole 256-byte head slices of the pools.  A token's sequence comes from a
+// binary search of query_start_loc (sequence s owns rows
+// [qsl[s], qsl[s+1])); without it, row t is sequence t's single token.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
+  constexpr int D = kHeadDim;
+  constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  const int64_t gid = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
+  const int64_t rows = (int64_t)p.total_tokens * p.num_kv_heads;
+  if (gid >= rows * kChunks) return;
+  const int dc = (int)(gid % kChunks);
+  const int64_t row = gid / kChunks;
+  const int h = (int)(row % p.num_kv_heads);
+  const int t = (int)(row / p.num_kv_heads);
+  int s = t, i = 0, qlen = 1;
+  if (p.query_start_loc) {
+    // last sequence whose first row is <= t (empty sequences own no rows)
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.query_start_loc[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    i = t - p.query_start_loc[s];
+    qlen = p.query_start_loc[s + 1] - p.query_start_loc[s];
+  }
+  const int L = p.context_lens[s];
+  const int pos = L - qlen + i;
+  if (pos < 0 || pos / kPage >= p.max_blocks) return;  // undefined input: skip
+  const int64_t page = p.block_tables[(int64_t)s * p.max_blocks + pos / kPage];
+  const int64_t dst = page * p.stride_page + (int64_t)(pos % kPage) * p.stride_token +
+                      (int64_t)h * p.stride_head + 8 * dc;
+  const int64_t src = row * D + 8 * dc;
+  *reinterpret_cast<uint4*>(p.k_pool + dst) = *reinterpret_cast<const uint4*>(p.k_new + src);
+  *reinterpret_cast<uint4*>(p.v_pool + dst) = *reinterpret_cast<const uint4*>(p.v_new + src);
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  const int64_t chunks = (int64_t)p.total_tokens * p.num_kv_heads * (kHeadDim / 8);
+  if (chunks == 0) return hipSuccess;
+  const int64_t grid = (chunks + kAppendThreads - 1) / kAppendThreads;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(kAppendThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

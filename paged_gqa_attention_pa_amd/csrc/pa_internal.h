@@ -97,6 +97,18 @@ struct TileMergeParams {
   int32_t q_tile, decode_rows_apart, tile_splits, out_f32;
 };
 
+struct AppendParams {
+  const uint16_t* k_new;    // [T, Hkv, D] bf16
+  const uint16_t* v_new;
+  const int32_t* query_start_loc;  // [B+1] or null (row t = sequence t)
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  int64_t stride_page, stride_token, stride_head;
+  int32_t num_seqs, num_kv_heads, max_blocks, total_tokens;
+};
+
 // Launchers: return hipSuccess or the launch error.  Shapes were checked.
 hipError_t launch_decode(const DecodeParams& p, int group, int waves, bool fused,
                          hipStream_t stream);
@@ -112,6 +124,7 @@ hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int g
 // Workgroups of the unified prefill kernel that fit on the device at once.
 int unified_resident(int group, bool precise_p);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream);
 
 }  // namespace pa

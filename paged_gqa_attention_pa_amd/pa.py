@@ -19,7 +19,7 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = ra
 PA_BF16, PA_FP32 = 0, 1
 
 EXPORTED = ["pa_select_tiles", "pa_workspace_size", "pa_decode", "pa_prefill",
-            "pa_splitkv_reduce", "pa_status_string"]
+            "pa_splitkv_reduce", "pa_cache_append", "pa_status_string"]
 
 
 class Problem(ctypes.Structure):
@@ -69,6 +69,7 @@ def load() -> ctypes.CDLL:
                                    ctypes.c_size_t, P]
         lib.pa_splitkv_reduce.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           P, ctypes.c_int32, P, P]
+        lib.pa_cache_append.argtypes = [PP(Problem), P, P, P, P, P, P, P, P]
         for f in EXPORTED[:-1]:
             getattr(lib, f).restype = ctypes.c_int
         lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -283,3 +284,55 @@ def splitkv_reduce(partial_o: torch.Tensor, partial_lse: torch.Tensor,
                                  odt, _ptr(lse), _stream(partial_o.device)),
            "pa_splitkv_reduce")
     return out
+
+
+def cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+                 v_pool: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                 query_start_loc: Optional[torch.Tensor] = None,
+                 problem: Optional[Problem] = None) -> None:
+    """pa_cache_append: k_new, v_new bf16 [T, Hkv, D]; writes them into the
+    pools at the newest q_len(s) positions of each sequence's context
+    (query_start_loc None: one token per sequence)."""
+    lib = load()
+    dev = k_new.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    for name, t, dt in [("k_new", k_new, torch.bfloat16), ("v_new", v_new, torch.bfloat16),
+                        ("k_pool", k_pool, torch.bfloat16), ("v_pool", v_pool, torch.bfloat16),
+                        ("block_tables", block_tables, torch.int32),
+                        ("context_lens", context_lens, torch.int32)]:
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, k_new on {dev}")
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}")
+    if (k_new.dim() != 3 or k_new.shape != v_new.shape or not k_new.is_contiguous()
+            or not v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous [T, Hkv, D] of one shape")
+    if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+        raise ValueError("K and V pools must share shape and strides")
+    if k_pool.dim() != 4 or tuple(k_new.shape[1:]) != tuple(k_pool.shape[2:]):
+        raise ValueError("pools must be [pages, P, Hkv, D] with k_new's Hkv and D")
+    if not block_tables.is_contiguous() or not context_lens.is_contiguous():
+        raise ValueError("block_tables and context_lens must be contiguous")
+    B = context_lens.shape[0]
+    if block_tables.shape[0] != B:
+        raise ValueError("block_tables needs one row per sequence")
+    T = k_new.shape[0]
+    if query_start_loc is None:
+        if T != B:
+            raise ValueError("without query_start_loc there is one token per sequence")
+    elif (query_start_loc.dtype != torch.int32 or query_start_loc.device != dev
+          or query_start_loc.shape[0] != B + 1 or not query_start_loc.is_contiguous()):
+        raise ValueError("query_start_loc must be contiguous int32 [B+1] on k_new's device")
+    if problem is None:
+        problem = make_problem(k_new, k_pool, block_tables, B, 1.0, 0, 1)
+    elif (problem.total_query_tokens != T or problem.num_seqs != B
+          or problem.num_kv_heads != k_pool.shape[2] or problem.head_dim != k_pool.shape[3]
+          or problem.page_size != k_pool.shape[1]
+          or problem.max_blocks_per_seq != block_tables.shape[1]
+          or (problem.kv_stride_page, problem.kv_stride_token, problem.kv_stride_head)
+          != tuple(int(x) for x in k_pool.stride()[:3])):
+        raise ValueError("problem does not match the tensors' shapes or strides")
+    _check(lib.pa_cache_append(ctypes.byref(problem), _ptr(k_new), _ptr(v_new),
+                               _ptr(query_start_loc), _ptr(block_tables), _ptr(context_lens),
+                               _ptr(k_pool), _ptr(v_pool), _stream(dev)), "pa_cache_append")

@@ -223,6 +223,19 @@ def generate(spec: WorkloadSpec, device="cpu", fill: str = "nan") -> Batch:
                  query_start_loc=qsl, query_lens=ql, used_pages=used)
 
 
+def new_kv(batch: Batch, seed: int):
+    """K and V rows of a batch's new tokens, as a paged append takes them:
+    bf16 [T, Hkv, D] each, fp32 standard normal rounded to bf16, K first,
+    from a generator seeded with ``seed`` on the batch's device."""
+    dev = batch.q.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    shape = (batch.num_tokens, batch.spec.num_kv_heads, batch.spec.head_dim)
+    k = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    return k, v
+
+
 def small_spec(name: str, seed: int, contexts: Sequence[int], queries: Sequence[int],
                num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                causal=True, pool_slack=7, decode_layout=None, logit_gain=1.0,

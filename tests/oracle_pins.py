@@ -18,6 +18,14 @@ What pins what:
   * merge_closed_form: the merge on hand-made partials.
   * gqa_equals_mha, prefill_row_equals_decode, q1_prefill_equals_decode,
     noncausal_prefill, empty_context: invariants and degenerate cases.
+  * append_round_trip: after a paged append, each sequence read back by
+    gathering its pages in table order shows the new rows at the end of the
+    context, the prefix unchanged, and exactly one changed slot per token.
+  * append_head_major_strides: a head-major pool through its strides.
+  * append_hand_case: slots worked out by hand on a two-sequence example.
+  * append_decode_steps_equal_chunk: token-by-token appends equal one chunk.
+  * append_then_attend: append followed by attention equals torch SDPA on the
+    dense context with the chunk's causal mask (pins where the chunk lands).
 """
 from __future__ import annotations
 
@@ -281,7 +289,167 @@ def empty_context(orc):
     assert np.all(np.isfinite(out[2:])) and np.all(np.isfinite(lse[2:]))
 
 
+def _append(orc, *args, **kw):
+    """The append oracle; a refused write (out-of-range position) fails the pin."""
+    try:
+        return orc.append(*args, **kw)
+    except RuntimeError as e:
+        raise AssertionError(str(e))
+
+
+def _random_bits(rng, shape):
+    return f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def _append_case(seed, P=4, Hkv=2, D=8, spare=3):
+    """Shuffled pages, mixed chunk lengths: a chunk crossing pages, a chunk that
+    is the whole context, a decode-like single token, an empty chunk, and a
+    chunk ending exactly on a page boundary."""
+    rng = np.random.default_rng(seed)
+    contexts = [7, 4, 13, 9, 8]
+    queries = [3, 4, 1, 0, 4]
+    blocks = [-(-c // P) for c in contexts]
+    npages = sum(blocks) + spare
+    order = rng.permutation(npages)
+    bt = np.full((len(contexts), max(blocks) + 1), 0, np.int32)
+    base = 0
+    for s, n in enumerate(blocks):
+        bt[s, :n] = order[base:base + n]
+        base += n
+    qsl = np.concatenate([[0], np.cumsum(queries)]).astype(np.int32)
+    return dict(rng=rng, P=P, Hkv=Hkv, D=D, npages=npages, bt=bt, contexts=contexts,
+                queries=queries, qsl=qsl, T=int(qsl[-1]))
+
+
+def _seq_view(pool, bt_row, nblocks, L):
+    """Logical rows [0, L) of one sequence of a [pages, P, Hkv, D] pool, by
+    gathering its pages in table order and flattening (page, slot)."""
+    return pool[bt_row[:nblocks]].reshape((-1,) + pool.shape[2:])[:L]
+
+
+def append_round_trip(orc):
+    c = _append_case(31)
+    P, Hkv, D, rng = c["P"], c["Hkv"], c["D"], c["rng"]
+    shape = (c["npages"], P, Hkv, D)
+    k0, v0 = _random_bits(rng, shape), _random_bits(rng, shape)
+    kn, vn = _random_bits(rng, (c["T"], Hkv, D)), _random_bits(rng, (c["T"], Hkv, D))
+    k1, v1 = _append(orc, k0, v0, P, (P * Hkv * D, Hkv * D, D), kn, vn, c["bt"],
+                     c["contexts"], c["qsl"])
+    for s, (L, q) in enumerate(zip(c["contexts"], c["queries"])):
+        nb = -(-L // P)
+        a, b = c["qsl"][s], c["qsl"][s + 1]
+        for pool1, pool0, new in ((k1, k0, kn), (v1, v0, vn)):
+            seq1 = _seq_view(pool1, c["bt"][s], nb, L)
+            seq0 = _seq_view(pool0, c["bt"][s], nb, L)
+            assert np.array_equal(seq1[L - q:], new[a:b])     # new rows at the context end
+            assert np.array_equal(seq1[:L - q], seq0[:L - q])  # the prefix is untouched
+    # nothing else moved: exactly one (page, slot) per new token changed
+    for pool1, pool0 in ((k1, k0), (v1, v0)):
+        changed = (pool1 != pool0).any(axis=(2, 3))
+        assert int(changed.sum()) == c["T"]
+
+
+def append_head_major_strides(orc):
+    """A pool laid out (page, kv head, slot, d) through its strides gives the
+    same rows as the default (page, slot, kv head, d) layout."""
+    c = _append_case(32)
+    P, Hkv, D, rng = c["P"], c["Hkv"], c["D"], c["rng"]
+    k0, v0 = _random_bits(rng, (c["npages"], P, Hkv, D)), _random_bits(rng, (c["npages"], P, Hkv, D))
+    kn, vn = _random_bits(rng, (c["T"], Hkv, D)), _random_bits(rng, (c["T"], Hkv, D))
+    args = (kn, vn, c["bt"], c["contexts"], c["qsl"])
+    k1, v1 = _append(orc, k0, v0, P, (P * Hkv * D, Hkv * D, D), *args)
+    kh = np.ascontiguousarray(k0.transpose(0, 2, 1, 3))
+    vh = np.ascontiguousarray(v0.transpose(0, 2, 1, 3))
+    k2, v2 = _append(orc, kh, vh, P, (Hkv * P * D, D, P * D), *args)
+    assert np.array_equal(k2.transpose(0, 2, 1, 3), k1)
+    assert np.array_equal(v2.transpose(0, 2, 1, 3), v1)
+
+
+def append_hand_case(orc):
+    """P = 4, one kv head, D = 2.  Sequence 0 holds 6 tokens, the last 3 new,
+    through table row [2, 0]: positions 3, 4, 5 are page 2 slot 3, page 0 slot
+    0, page 0 slot 1.  Sequence 1 holds 1 token, new, through [1, 1]: position
+    0 is page 1 slot 0."""
+    P, D = 4, 2
+    k0 = np.zeros((3, P, 1, D), np.uint16)
+    v0 = np.full((3, P, 1, D), 7, np.uint16)
+    kn = np.array([[[11, 12]], [[21, 22]], [[31, 32]], [[41, 42]]], np.uint16)
+    vn = kn + 100
+    k1, v1 = _append(orc, k0, v0, P, (P * D, D, D), kn, vn,
+                     np.array([[2, 0], [1, 1]], np.int32), [6, 1],
+                     np.array([0, 3, 4], np.int32))
+    want_k, want_v = k0.copy(), v0.copy()
+    for (page, slot), row in {(2, 3): 0, (0, 0): 1, (0, 1): 2, (1, 0): 3}.items():
+        want_k[page, slot, 0] = kn[row, 0]
+        want_v[page, slot, 0] = vn[row, 0]
+    assert np.array_equal(k1, want_k) and np.array_equal(v1, want_v)
+
+
+def append_decode_steps_equal_chunk(orc):
+    """Appending a chunk token by token (one-token-per-sequence layout, the
+    context growing by one each step) fills the same slots as one chunk."""
+    c = _append_case(33)
+    P, Hkv, D, rng = c["P"], c["Hkv"], c["D"], c["rng"]
+    strides = (P * Hkv * D, Hkv * D, D)
+    k0, v0 = _random_bits(rng, (c["npages"], P, Hkv, D)), _random_bits(rng, (c["npages"], P, Hkv, D))
+    kn, vn = _random_bits(rng, (c["T"], Hkv, D)), _random_bits(rng, (c["T"], Hkv, D))
+    k1, v1 = _append(orc, k0, v0, P, strides, kn, vn, c["bt"], c["contexts"], c["qsl"])
+    ks, vs = k0, v0
+    qmax = max(c["queries"])
+    for step in range(qmax):
+        # every sequence still adding tokens gets its next one; the others re-append
+        # their last prefix row unchanged (a no-op write of the value already there)
+        rows_k, rows_v, lens = [], [], []
+        for s, (L, q) in enumerate(zip(c["contexts"], c["queries"])):
+            if step < q:
+                r = c["qsl"][s] + step
+                rows_k.append(kn[r])
+                rows_v.append(vn[r])
+                lens.append(L - q + step + 1)
+            else:
+                lens.append(0)  # context shorter than its one token: nothing written
+                rows_k.append(np.zeros((Hkv, D), np.uint16))
+                rows_v.append(np.zeros((Hkv, D), np.uint16))
+        ks, vs = _append(orc, ks, vs, P, strides, np.stack(rows_k), np.stack(rows_v), c["bt"],
+                         lens, None)
+    assert np.array_equal(ks, k1) and np.array_equal(vs, v1)
+
+
+def append_then_attend(orc):
+    """Append a chunk, then attend: equals torch SDPA over the dense context
+    (cached prefix followed by the new rows) with the chunk's causal mask."""
+    import oracle as oracle_mod
+    P, Hq, Hkv, D = 4, 4, 2, 8
+    L, q = 23, 7
+    rng = np.random.default_rng(34)
+    npages = -(-L // P) + 2
+    bt = rng.permutation(npages)[None, :].astype(np.int32)
+    shape = (npages, P, Hkv, D)
+    k0, v0 = _random_bits(rng, shape), _random_bits(rng, shape)
+    kn, vn = _random_bits(rng, (q, Hkv, D)), _random_bits(rng, (q, Hkv, D))
+    qb = _random_bits(rng, (q, Hq, D))
+    strides = (P * Hkv * D, Hkv * D, D)
+    qsl = np.array([0, q], np.int32)
+    k1, v1 = _append(orc, k0, v0, P, strides, kn, vn, bt, [L], qsl)
+    inp = oracle_mod.PagedInputs(q=qb, k_pool=k1, v_pool=v1, block_tables=bt,
+                                 context_lens=np.array([L], np.int32), query_start_loc=qsl,
+                                 num_kv_heads=Hkv, page_size=P, strides=strides,
+                                 scale=0.25, causal=True)
+    out, _ = orc.attention(inp)
+    nb = -(-L // P)
+    kd = np.concatenate([bits_to_f64(_seq_view(k0, bt[0], nb, L)[:L - q]), bits_to_f64(kn)])
+    vd = np.concatenate([bits_to_f64(_seq_view(v0, bt[0], nb, L)[:L - q]), bits_to_f64(vn)])
+    G = Hq // Hkv
+    mask = np.tril(np.ones((q, L), bool), k=L - q)
+    ref = _sdpa(bits_to_f64(qb), np.repeat(kd, G, axis=1), np.repeat(vd, G, axis=1), 0.25,
+                mask=mask)
+    np.testing.assert_allclose(out.reshape(q, Hq, D), ref, rtol=0, atol=1e-12)
+
+
+APPEND_PINS = [append_round_trip, append_head_major_strides, append_hand_case,
+               append_decode_steps_equal_chunk, append_then_attend]
+
 ALL_PINS = [dense_decode_sdpa, dense_causal_sdpa, golden_two_token, permutation_invariance,
             dominant_logit, uniform_v, q_zero, single_token, split_merge, merge_closed_form,
             gqa_equals_mha, prefill_row_equals_decode, q1_prefill_equals_decode,
-            noncausal_prefill, empty_context]
+            noncausal_prefill, empty_context] + APPEND_PINS

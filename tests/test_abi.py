@@ -153,6 +153,30 @@ def test_compute_calls_reject_before_launch(lib):
     assert lib.pa_splitkv_reduce(fake, fake, 0, 2, 128, fake, pa.PA_FP32, nul, nul) == pa.PA_OK
 
 
+def test_cache_append_rejects_before_launch(lib):
+    fake = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10008)
+    nul = None
+
+    def call(pb, k_new=fake, v_new=fake, qsl=nul, bt=fake, cl=fake, kp=fake, vp=fake):
+        return lib.pa_cache_append(ctypes.byref(pb), k_new, v_new, qsl, bt, cl, kp, vp, nul)
+
+    pb = _problem()
+    assert call(pb, k_new=nul) == pa.PA_ERR_INVALID_ARG
+    assert call(pb, vp=nul) == pa.PA_ERR_INVALID_ARG
+    assert call(pb, bt=nul) == pa.PA_ERR_INVALID_ARG
+    assert call(pb, v_new=mis) == pa.PA_ERR_INVALID_ARG
+    assert call(pb, kp=mis) == pa.PA_ERR_INVALID_ARG
+    # one token per sequence unless query_start_loc is given
+    assert call(_problem(total_query_tokens=9)) == pa.PA_ERR_INVALID_ARG
+    assert call(_problem(head_dim=64, kv_stride_head=64)) == pa.PA_ERR_UNSUPPORTED
+    assert call(_problem(page_size=32)) == pa.PA_ERR_UNSUPPORTED
+    assert call(_problem(kv_stride_token=12)) == pa.PA_ERR_INVALID_ARG
+    # nothing to write: no launch
+    assert call(_problem(num_seqs=0, total_query_tokens=0)) == pa.PA_OK
+    assert call(_problem(total_query_tokens=0), qsl=fake) == pa.PA_OK
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert pa.status_string(s)

@@ -1,0 +1,223 @@
+"""GPU parity of the paged KV append (pa_cache_append) against the oracle.
+
+Appends copy bits, so every case must match bit for bit: the pages the new
+tokens land in are compared whole with the oracle's append of the same
+pages, and across the whole pool exactly one (page, slot) per new token may
+change.  The end-to-end cases append a chunk (or one decode token per
+sequence) and then attend over the pages, against the oracle's append
+followed by the oracle's attention, to the attention tolerances.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_gqa_attention_pa_amd import pa, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    return torch.device("cuda:0")
+
+
+def _bits(t):
+    return workloads.bf16_bits(t)
+
+
+def _landing_pages(b):
+    """Page ids holding the new tokens' positions (the last q_s of each
+    context), and per sequence the block range they cover."""
+    P = b.spec.page_size
+    bt = b.block_tables.cpu().numpy()
+    ctx = b.context_lens.cpu().numpy()
+    pages, ranges = [], []
+    for s, q in enumerate(b.query_lens):
+        L = int(ctx[s])
+        if q == 0:
+            ranges.append(range(0))
+            continue
+        r = range((L - q) // P, (L - 1) // P + 1)
+        ranges.append(r)
+        pages += [int(bt[s, blk]) for blk in r]
+    return np.unique(np.array(pages, dtype=np.int64)), ranges
+
+
+def append_and_check(b, kn, vn, label):
+    """Append on the GPU, then compare with the oracle bit for bit."""
+    qsl = b.query_start_loc
+    before_k, before_v = b.k_pool.clone(), b.v_pool.clone()
+    pa.cache_append(kn, vn, b.k_pool, b.v_pool, b.block_tables, b.context_lens, qsl)
+    torch.cuda.synchronize()
+    T = b.num_tokens
+    for after, before in ((b.k_pool, before_k), (b.v_pool, before_v)):
+        changed = (after.view(torch.int16) != before.view(torch.int16)).any(dim=3).any(dim=2)
+        n = int(changed.sum().item())
+        assert n == T, f"{label}: {n} slots changed, {T} new tokens"
+    # the oracle on just the landing pages, with the table remapped to them
+    sel, ranges = _landing_pages(b)
+    remap = {int(p): i for i, p in enumerate(sel)}
+    bt = b.block_tables.cpu().numpy()
+    bt_c = np.zeros_like(bt)
+    for s, r in enumerate(ranges):
+        for blk in r:
+            bt_c[s, blk] = remap[int(bt[s, blk])]
+    sel_t = torch.from_numpy(sel).to(b.k_pool.device)
+    P, Hkv, D = b.spec.page_size, b.spec.num_kv_heads, b.spec.head_dim
+    k_exp, v_exp = oracle.append(
+        _bits(before_k[sel_t].contiguous()), _bits(before_v[sel_t].contiguous()), P,
+        (P * Hkv * D, Hkv * D, D), _bits(kn), _bits(vn), bt_c, b.context_lens.cpu().numpy(),
+        None if qsl is None else qsl.cpu().numpy())
+    k_got = _bits(b.k_pool[sel_t].contiguous())
+    v_got = _bits(b.v_pool[sel_t].contiguous())
+    assert np.array_equal(k_got, k_exp), f"{label}: K pages differ"
+    assert np.array_equal(v_got, v_exp), f"{label}: V pages differ"
+    log(f"{label}: {T} tokens, {sel.size} landing pages bit-exact")
+
+
+APPEND_CASES = [
+    # name, contexts, queries, Hq, Hkv
+    ("ragged", [1, 15, 16, 17, 300, 1000, 0, 2049, 33], [1, 15, 3, 17, 100, 1, 0, 2049, 16], 32, 8),
+    ("decode", [5, 16, 17, 1, 4000, 32, 700], [1] * 7, 32, 8),
+    ("hkv1", [100, 33, 257], [40, 33, 2], 8, 1),
+    ("hkv2", [100, 33, 257], [100, 1, 17], 16, 2),
+    ("empty_chunks", [64, 10, 80], [0, 0, 16], 32, 8),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql,hq,hkv", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_append_small(dev, name, ctx, ql, hq, hkv):
+    log(f"[append {name}]")
+    spec = workloads.small_spec(f"app_{name}", seed=300 + len(ctx) + hkv, contexts=ctx,
+                                queries=ql, num_q_heads=hq, num_kv_heads=hkv, pool_slack=9)
+    b = workloads.generate(spec, dev)
+    kn, vn = workloads.new_kv(b, seed=400 + hkv)
+    append_and_check(b, kn, vn, f"append {name}")
+
+
+def test_append_decode_layout_matches_chunk_layout(dev):
+    """query_start_loc = NULL (one token each) and an explicit [0, 1, .., B]
+    give the same pools."""
+    log("[append decode layout]")
+    spec = workloads.small_spec("app_dl", seed=311, contexts=[9, 16, 1, 300, 4097],
+                                queries=[1] * 5)
+    b = workloads.generate(spec, dev)
+    kn, vn = workloads.new_kv(b, seed=411)
+    k2, v2 = b.k_pool.clone(), b.v_pool.clone()
+    append_and_check(b, kn, vn, "append decode layout")
+    qsl = torch.arange(b.num_seqs + 1, dtype=torch.int32, device=dev)
+    pa.cache_append(kn, vn, k2, v2, b.block_tables, b.context_lens, qsl)
+    torch.cuda.synchronize()
+    assert torch.equal(k2.view(torch.int16), b.k_pool.view(torch.int16))
+    assert torch.equal(v2.view(torch.int16), b.v_pool.view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["head_major", "padded"])
+def test_append_strided_pool(dev, layout):
+    """Pools seen through strides: (page, kv head, slot, d) storage, or a
+    token-major pool with padded head and page strides."""
+    log(f"[append strided {layout}]")
+    ctx, ql = [70, 16, 300], [30, 16, 1]
+    spec = workloads.small_spec(f"app_{layout}", seed=320, contexts=ctx, queries=ql)
+    b = workloads.generate(spec, dev)
+    kn, vn = workloads.new_kv(b, seed=420)
+    npg, P, Hkv, D = b.k_pool.shape
+    if layout == "head_major":
+        ks = b.k_pool.permute(0, 2, 1, 3).contiguous()
+        vs = b.v_pool.permute(0, 2, 1, 3).contiguous()
+        kview, vview = ks.permute(0, 2, 1, 3), vs.permute(0, 2, 1, 3)
+        strides = (Hkv * P * D, D, P * D)
+    else:
+        ks = torch.full((npg, P, Hkv + 1, D + 8), float("nan"), dtype=torch.bfloat16, device=dev)
+        vs = ks.clone()
+        ks[:, :, :Hkv, :D] = b.k_pool
+        vs[:, :, :Hkv, :D] = b.v_pool
+        kview, vview = ks[:, :, :Hkv, :D], vs[:, :, :Hkv, :D]
+        strides = tuple(int(x) for x in ks.stride()[:3])
+    assert tuple(int(x) for x in kview.stride()[:3]) == strides
+    k_exp, v_exp = oracle.append(_bits(ks), _bits(vs), P, strides, _bits(kn), _bits(vn),
+                                 b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy(),
+                                 b.query_start_loc.cpu().numpy())
+    pa.cache_append(kn, vn, kview, vview, b.block_tables, b.context_lens, b.query_start_loc)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(ks), k_exp) and np.array_equal(_bits(vs), v_exp)
+
+
+@pytest.mark.parametrize("name", ["prefill_chunk2048", "decode_b64", "mixed_unified"])
+def test_append_full_size(dev, name):
+    """The benchmark workloads' own shapes and launch: every new token of
+    the batch appended at once."""
+    log(f"[append full size {name}]")
+    b = workloads.generate(workloads.WORKLOADS[name], dev)
+    kn, vn = workloads.new_kv(b, seed=430)
+    append_and_check(b, kn, vn, f"append {name}")
+
+
+def _oracle_attention_after_append(b, kn, vn, k_bits, v_bits, rows=None):
+    """Oracle append on host copies of the pre-append pools, then oracle
+    attention over the result."""
+    qsl = None if b.query_start_loc is None else b.query_start_loc.cpu().numpy()
+    kp, vp = oracle.append(k_bits, v_bits, b.spec.page_size, b.kv_strides(), _bits(kn),
+                           _bits(vn), b.block_tables.cpu().numpy(),
+                           b.context_lens.cpu().numpy(), qsl)
+    inp = oracle.PagedInputs(q=_bits(b.q), k_pool=kp, v_pool=vp,
+                             block_tables=b.block_tables.cpu().numpy(),
+                             context_lens=b.context_lens.cpu().numpy(), query_start_loc=qsl,
+                             num_kv_heads=b.spec.num_kv_heads, page_size=b.spec.page_size,
+                             strides=b.kv_strides(), scale=b.spec.scale, causal=b.spec.causal)
+    return oracle.attention(inp, rows=rows)
+
+
+def _assert_close(got, ref, label, tol=2e-3):
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    log(f"{label}: max|err|={err:.3e} (tol {tol})")
+    assert err <= tol, f"{label}: max|err| {err} > {tol}"
+
+
+def test_append_then_prefill(dev):
+    """A chunk appended into its pages, then attended (fp32 output)."""
+    log("[append then prefill]")
+    spec = workloads.small_spec("app_pf", seed=330, contexts=[3072, 700, 40, 1],
+                                queries=[2048, 100, 40, 1])
+    b = workloads.generate(spec, dev)
+    kn, vn = workloads.new_kv(b, seed=440)
+    k_bits, v_bits = _bits(b.k_pool), _bits(b.v_pool)
+    pa.cache_append(kn, vn, b.k_pool, b.v_pool, b.block_tables, b.context_lens,
+                    b.query_start_loc)
+    out = pa.prefill(b.q, b.query_start_loc, b.k_pool, b.v_pool, b.block_tables,
+                     b.context_lens, spec.scale, b.max_context_len, b.max_query_len,
+                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(b.num_tokens * spec.num_q_heads, 4096, replace=False))
+    ref, _ = _oracle_attention_after_append(b, kn, vn, k_bits, v_bits, rows=rows)
+    got = out.cpu().numpy().reshape(-1, spec.head_dim)[rows]
+    _assert_close(got, ref, "append+prefill")
+
+
+def test_append_then_decode(dev):
+    """One new token per sequence appended, then a decode step over it."""
+    log("[append then decode]")
+    spec = workloads.small_spec("app_dec", seed=331, contexts=[1, 17, 4000, 513, 16],
+                                queries=[1] * 5)
+    b = workloads.generate(spec, dev)
+    kn, vn = workloads.new_kv(b, seed=441)
+    k_bits, v_bits = _bits(b.k_pool), _bits(b.v_pool)
+    pa.cache_append(kn, vn, b.k_pool, b.v_pool, b.block_tables, b.context_lens)
+    out = pa.decode(b.q, b.k_pool, b.v_pool, b.block_tables, b.context_lens, spec.scale,
+                    b.max_context_len, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, _ = _oracle_attention_after_append(b, kn, vn, k_bits, v_bits)
+    _assert_close(out.cpu().numpy().reshape(-1, spec.head_dim), ref, "append+decode")

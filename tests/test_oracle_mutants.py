@@ -31,6 +31,14 @@ MUTANTS = {
     "v_read_from_k": ("const uint16_t *vrow = j->v_pool", "const uint16_t *vrow = j->k_pool"),
     "split_drops_token": ("int64_t e = b + j->split_tokens;",
                           "int64_t e = b + j->split_tokens - 1;"),
+    "append_position_shifted": ("int64_t pos = L - q_s + i;", "int64_t pos = L - q_s + i + 1;"),
+    "append_slot_is_block": ("int64_t slot = pos % page_size;", "int64_t slot = block;"),
+    "append_head_row_dropped": ("((first + i) * num_kv_heads + h)", "((first + i) + h)"),
+    "append_v_from_k": ("v_pool[dst + d] = v_new[src + d];", "v_pool[dst + d] = k_new[src + d];"),
+    "append_decode_first_row": ("first = query_start_loc ? query_start_loc[s] : s;",
+                                "first = query_start_loc ? query_start_loc[s] : 0;"),
+    "append_page_from_block": ("int64_t page = block_tables[(int64_t)s * max_blocks + block];",
+                               "int64_t page = block;"),
     "query_row_head_swapped": ("j->q + (t * Hq + h) * (int64_t)D",
                                "j->q + (t * Hq + (Hq - 1 - h)) * (int64_t)D"),
 }
