@@ -48,8 +48,11 @@ PREFILL_TRAFFIC = {
     "mixed_unified": 643105086,
 }
 
-# The same for one pa_cache_append call (append_kernel).
-APPEND_TRAFFIC = {}
+# The same for one pa_cache_append call.
+APPEND_TRAFFIC = {
+    # append_kernel (profiles/append_prefill_chunk2048_hbm_counters.md)
+    "prefill_chunk2048": 67206455,
+}
 
 
 def note(msg):
@@ -385,6 +388,7 @@ def main():
         app = bench_append(torch, pa, workloads, dev, args.steps, args.warmup,
                            name=args.prefill_workload)
         note(f"append: {app['us_per_step']} us, {app['value']} GB/s")
+        calibrate_copy(torch, dev, args.calibrate_copy)
         print(json.dumps(app), flush=True)
         return
     if args.prefill_only:

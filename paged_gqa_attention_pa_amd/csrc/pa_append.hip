@@ -8,6 +8,10 @@
 // whole 256-byte head slices of the pools.  A token's sequence comes from a
 // binary search of query_start_loc (sequence s owns rows
 // [qsl[s], qsl[s+1])); without it, row t is sequence t's single token.
+// The pool writes are nontemporal: nothing in this kernel reads them again,
+// and marking them streaming measured 5.2 TB/s against 3.7 TB/s for plain
+// stores on a 67 MB append (loads stay ordinary: nontemporal loads did not
+// help).
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -16,6 +20,7 @@ namespace pa {
 namespace {
 
 constexpr int kAppendThreads = 256;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
   constexpr int D = kHeadDim;
@@ -46,8 +51,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
   const int64_t dst = page * p.stride_page + (int64_t)(pos % kPage) * p.stride_token +
                       (int64_t)h * p.stride_head + 8 * dc;
   const int64_t src = row * D + 8 * dc;
-  *reinterpret_cast<uint4*>(p.k_pool + dst) = *reinterpret_cast<const uint4*>(p.k_new + src);
-  *reinterpret_cast<uint4*>(p.v_pool + dst) = *reinterpret_cast<const uint4*>(p.v_new + src);
+  const u32x4 k = *reinterpret_cast<const u32x4*>(p.k_new + src);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p.v_new + src);
+  __builtin_nontemporal_store(k, reinterpret_cast<u32x4*>(p.k_pool + dst));
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.v_pool + dst));
 }
 
 }  // namespace
