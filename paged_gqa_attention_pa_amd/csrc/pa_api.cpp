@@ -71,6 +71,14 @@ struct Workspace {
   size_t o_off, lse_off, ctr_off, cnt_off, dec_total, to_off, tlse_off, total;
 };
 
+// Short query runs (speculative-decode verification): every sequence of the
+// batch has at most max_query_len >= 2 tokens and max_query_len * G <= 64,
+// so a (sequence, kv head) unit is one Q-block of at most 64 rows.
+bool verify_path(const pa_problem* pb) {
+  const int G = pb->num_q_heads / pb->num_kv_heads;
+  return pb->max_query_len >= 2 && pa::verify_row_blocks(G, pb->max_query_len) > 0;
+}
+
 bool even_grid(const pa_tiles* t) {
   return t->num_splits > 1 && (t->variant & pa::kVariantEvenWork) != 0;
 }
@@ -79,16 +87,19 @@ Workspace workspace_layout(const pa_problem* pb, const pa_tiles* t) {
   Workspace w{0, 0, 0, 0, 0, 0, 0, 0};
   const int64_t D = pb->head_dim;
   const int S = t->num_splits;
-  if (S > 1) {
-    const int64_t rows = (int64_t)pb->num_seqs * pb->num_q_heads;
-    const int64_t slots = S + (even_grid(t) ? 1 : 0);
+  const bool verify = verify_path(pb);
+  if (S > 1 || verify) {
+    // short query runs: (token, head) rows, always the even-work grid
+    const int64_t rows = (int64_t)(verify ? pb->total_query_tokens : pb->num_seqs) *
+                         pb->num_q_heads;
+    const int64_t slots = S + ((verify || even_grid(t)) ? 1 : 0);
     const size_t units = (size_t)((int64_t)pb->num_seqs * pb->num_kv_heads);
     w.lse_off = align_up((size_t)(rows * slots * D) * sizeof(float));
     w.ctr_off = w.lse_off + align_up((size_t)(rows * slots) * sizeof(float));
     w.cnt_off = w.ctr_off + align_up(units * sizeof(int32_t));
     w.dec_total = w.cnt_off + align_up(units * sizeof(int32_t));
   }
-  const int ts = tile_splits_of(pb, t);
+  const int ts = verify ? 1 : tile_splits_of(pb, t);
   w.total = w.dec_total;
   if (ts > 1) {
     const int64_t rows = (int64_t)pb->total_query_tokens * pb->num_q_heads;
@@ -106,6 +117,69 @@ pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; 
 bool may_hold_decode_rows(const pa_problem* pb) {
   return pb->max_query_len <= 1 ||
          (int64_t)pb->total_query_tokens < (int64_t)pb->num_seqs * pb->max_query_len;
+}
+
+// pa_prefill for short query runs: the even-work grid over every
+// (sequence, kv head) unit with one Q-block per unit, then the merge of the
+// units cut into several pieces.  Arguments were checked by the caller.
+pa_status prefill_short_runs(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                             const int32_t* query_start_loc, const void* k_pool,
+                             const void* v_pool, const int32_t* block_tables,
+                             const int32_t* context_lens, void* out, float* lse, char* ws,
+                             const Workspace& wl, hipStream_t stream) {
+  const int G = problem->num_q_heads / problem->num_kv_heads;
+  const int S = tiles->num_splits;
+  const int rb = pa::verify_row_blocks(G, problem->max_query_len);
+  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
+  pa::DecodeParams d;
+  d.q = static_cast<const uint16_t*>(q);
+  d.k_pool = static_cast<const uint16_t*>(k_pool);
+  d.v_pool = static_cast<const uint16_t*>(v_pool);
+  d.block_tables = block_tables;
+  d.context_lens = context_lens;
+  d.out = out;
+  d.lse = lse;
+  d.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+  d.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+  d.counters = reinterpret_cast<int32_t*>(ws + wl.ctr_off);
+  d.piece_counts = reinterpret_cast<int32_t*>(ws + wl.cnt_off);
+  d.query_start_loc = query_start_loc;
+  d.stride_page = problem->kv_stride_page;
+  d.stride_token = problem->kv_stride_token;
+  d.stride_head = problem->kv_stride_head;
+  d.num_seqs = problem->num_seqs;
+  d.num_q_heads = problem->num_q_heads;
+  d.num_kv_heads = problem->num_kv_heads;
+  d.max_blocks = problem->max_blocks_per_seq;
+  d.num_splits = S + 1;
+  const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
+  d.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
+  d.max_tiles = ntiles;
+  d.even_min_tiles = d.tiles_per_split;
+  d.scale_log2 = problem->scale * pa::kLog2eHost;
+  d.out_f32 = problem->out_dtype == PA_FP32;
+  d.causal = problem->causal;
+  const int nw = pa::verify_resident(G, rb, precise);
+  if (nw <= 0) return PA_ERR_HIP;
+  pa_status st = from_hip(pa::launch_verify(d, G, rb, precise, nw, stream));
+  if (st != PA_OK) return st;
+  pa::ReduceParams r;
+  r.part_o = d.part_o;
+  r.part_lse = d.part_lse;
+  r.out = out;
+  r.lse = lse;
+  r.rows = problem->total_query_tokens * problem->num_q_heads;
+  r.num_splits = d.num_splits;
+  r.head_dim = problem->head_dim;
+  r.out_f32 = d.out_f32;
+  r.query_start_loc = query_start_loc;
+  r.num_q_heads = problem->num_q_heads;
+  r.piece_counts = d.piece_counts;
+  r.context_lens = context_lens;
+  r.group = G;
+  r.token_rows = 1;
+  r.num_seqs = problem->num_seqs;
+  return from_hip(pa::launch_reduce(r, stream));
 }
 
 }  // namespace
@@ -148,6 +222,16 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     t.q_tokens_per_tile = 1;
     t.num_splits = dc.splits;
     t.variant = dc.variant;
+  } else if (verify_path(problem)) {
+    // short query runs: the decode grid choice, each unit one Q-block of
+    // max_query_len tokens x G heads, 4 wavefronts, even-work grid
+    t.kv_tile = pa::kDecodeTile;
+    t.waves_per_wg = 4;
+    t.q_tokens_per_tile = problem->max_query_len;
+    t.num_splits = dc.splits;
+    t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
+                pa::kVariantSeparateMerge | pa::kVariantEvenWork;
+    t.tile_splits = 0;
   } else {
     t.kv_tile = 32;
     t.waves_per_wg = 8;
@@ -232,6 +316,7 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   p.even_min_tiles = p.tiles_per_split;
   p.scale_log2 = problem->scale * pa::kLog2eHost;
   p.out_f32 = problem->out_dtype == PA_FP32;
+  p.causal = problem->causal;
   const bool separate = S > 1 && (tiles->variant & pa::kVariantSeparateMerge) != 0;
   if (even) {
     const int nw = pa::decode_even_resident(G, waves);
@@ -255,6 +340,8 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
     r.piece_counts = even ? p.piece_counts : nullptr;
     r.context_lens = context_lens;
     r.group = G;
+    r.token_rows = 0;
+    r.num_seqs = problem->num_seqs;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -273,9 +360,11 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PA_ERR_INVALID_ARG;
-  // G = 16 has no decode workgroups in this launch: its single-token
-  // sequences take the prefill tiles
-  const bool decode_rows = may_hold_decode_rows(problem) && G <= 8;
+  // A batch of single-token sequences runs on the decode kernels.  In the
+  // unified launch G = 16 has no decode workgroups: its single-token
+  // sequences take the prefill tiles.
+  const bool decode_only = problem->max_query_len <= 1;
+  const bool decode_rows = decode_only || (may_hold_decode_rows(problem) && G <= 8);
   const int S = decode_rows ? tiles->num_splits : 1;
   const bool even = decode_rows && even_grid(tiles);
   const int TS = tile_splits_of(problem, tiles);
@@ -284,6 +373,9 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
                        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0 || problem->total_query_tokens == 0) return PA_OK;
+  if (verify_path(problem))
+    return prefill_short_runs(problem, tiles, q, query_start_loc, k_pool, v_pool, block_tables,
+                              context_lens, out, lse, static_cast<char*>(workspace), wl, stream);
   const int qt = 256 / G;
   const float scale_log2 = problem->scale * pa::kLog2eHost;
   const int out_f32 = problem->out_dtype == PA_FP32;
@@ -352,10 +444,47 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.even_min_tiles = d.tiles_per_split;
   d.scale_log2 = scale_log2;
   d.out_f32 = out_f32;
+  d.causal = problem->causal;
 
+  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
+  if (decode_only) {
+    // every sequence is a decode row: the decode kernels alone (measured on a
+    // batch of 64: 231 us against 267 us for the decode part of the unified
+    // kernel, whose registers allow one 512-thread workgroup per CU); splits
+    // are always merged by the separate kernel here
+    const int waves = tiles->waves_per_wg;
+    if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
+    if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
+    if (even) {
+      const int nw = pa::decode_even_resident(G, waves);
+      if (nw <= 0) return PA_ERR_HIP;
+      if ((st = from_hip(pa::launch_decode_even(d, G, waves, nw, stream))) != PA_OK) return st;
+    } else if ((st = from_hip(pa::launch_decode(d, G, waves, false, stream))) != PA_OK) {
+      return st;
+    }
+    if (S > 1) {
+      pa::ReduceParams r;
+      r.part_o = d.part_o;
+      r.part_lse = d.part_lse;
+      r.out = out;
+      r.lse = lse;
+      r.rows = problem->num_seqs * problem->num_q_heads;
+      r.num_splits = d.num_splits;
+      r.head_dim = problem->head_dim;
+      r.out_f32 = out_f32;
+      r.query_start_loc = query_start_loc;
+      r.num_q_heads = problem->num_q_heads;
+      r.piece_counts = d.piece_counts;
+      r.context_lens = context_lens;
+      r.group = G;
+      r.token_rows = 0;
+      r.num_seqs = problem->num_seqs;
+      st = from_hip(pa::launch_reduce(r, stream));
+    }
+    return st;
+  }
   // static grid: sum over sequences of ceil(q_len / qt) <= ceil(T / qt) + B
   const int64_t nx = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
-  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
   int64_t n_dec = decode_rows ? (int64_t)problem->num_seqs * problem->num_kv_heads * S : 0;
   if (even) {
     n_dec = pa::unified_resident(G, precise);
@@ -395,6 +524,8 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     r.piece_counts = d.piece_counts;
     r.context_lens = context_lens;
     r.group = G;
+    r.token_rows = 0;
+    r.num_seqs = problem->num_seqs;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -455,6 +586,8 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
   r.piece_counts = nullptr;
   r.context_lens = nullptr;
   r.group = 1;
+  r.token_rows = 0;
+  r.num_seqs = 0;
   return from_hip(pa::launch_reduce(r, stream));
 }
 

@@ -4,7 +4,7 @@
 // number of workgroups sharing all tiles equally (decode_even_body).
 #include <atomic>
 
-#include "pa_decode_body.h"
+#include "pa_even_grid.h"
 
 namespace pa {
 

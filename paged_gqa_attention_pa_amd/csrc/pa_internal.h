@@ -40,6 +40,7 @@ struct DecodeParams {
   int32_t* piece_counts;    // even-work grid: [B*Hkv] pieces per unit
   float scale_log2;         // scale * log2(e)
   int32_t out_f32;
+  int32_t causal;           // short query runs: causal within the run
 };
 
 struct PrefillParams {
@@ -83,6 +84,11 @@ struct ReduceParams {
   const int32_t* piece_counts;
   const int32_t* context_lens;
   int32_t group;
+  // Short query runs: rows are (token, q head) pairs of every sequence,
+  // output row = partial row; the sequence of a row (for piece_counts and
+  // context_lens) is found in query_start_loc.
+  int32_t token_rows;
+  int32_t num_seqs;
 };
 
 // Merge of split query tiles: one workgroup per (query tile, kv head) of the
@@ -124,6 +130,13 @@ hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int g
 // Workgroups of the unified prefill kernel that fit on the device at once.
 int unified_resident(int group, bool precise_p);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+// Short query runs (1 <= q_s, q_s * G <= 64): 16-row blocks per unit (1, 2
+// or 4; 0 when max_query_len * G exceeds 64), resident workgroups of that
+// kernel, and the even-work launch of nw workgroups.
+int verify_row_blocks(int group, int max_query_len);
+int verify_resident(int group, int rb, bool precise_p);
+hipError_t launch_verify(const DecodeParams& p, int group, int rb, bool precise_p, int nw,
+                         hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream);
 

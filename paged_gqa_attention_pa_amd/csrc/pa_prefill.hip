@@ -8,7 +8,7 @@
 // partials, merged afterwards by tile_merge_kernel (pa_reduce.hip).
 #include <atomic>
 
-#include "pa_decode_body.h"
+#include "pa_even_grid.h"
 #include "pa_prefill_body.h"
 
 namespace pa {

@@ -44,7 +44,18 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   int64_t orow = row;
-  if (p.query_start_loc) {  // mixed batch: merge the single-token sequences only
+  int b = row / p.num_q_heads;  // sequence of the row
+  if (p.query_start_loc && p.token_rows) {
+    // rows are (token, head) pairs: the last sequence starting at or before
+    // the token owns it (empty sequences own no tokens)
+    const int t = row / p.num_q_heads;
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.query_start_loc[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  } else if (p.query_start_loc) {  // mixed batch: merge the single-token sequences only
     const int s = row / p.num_q_heads;
     const int q0 = p.query_start_loc[s];
     if (p.query_start_loc[s + 1] - q0 != 1) return;
@@ -56,7 +67,6 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
   if (p.piece_counts) {
     // even-work decode grid: an empty context has no pieces (O = 0,
     // lse = -inf); a unit of one piece was written directly
-    const int b = row / p.num_q_heads;
     const int u = b * (p.num_q_heads / p.group) + (row % p.num_q_heads) / p.group;
     if (p.context_lens[b] <= 0) {
       for (int d = tid; d < D; d += kThreads) {

@@ -1,0 +1,99 @@
+// Short-query-run kernels for gfx950 (speculative-decode verification
+// batches: every sequence has 1 <= q_s query tokens with q_s * G <= 64): the
+// even-work grid of the decode path driving verify_body (pa_verify_body.h),
+// one instantiation per (G, row blocks RB, precise P).  Rows are
+// (token, q head) pairs: partials are [T*Hq, slots, D].
+#include <atomic>
+
+#include "pa_even_grid.h"
+
+namespace pa {
+
+namespace {
+
+using decode_detail::decode_even_body;
+using verify_detail::verify_smem_floats;
+
+constexpr int kVerifyWaves = 4;
+
+// Two workgroups per CU where the row blocks allow (RB <= 2), so that two
+// wavefronts per SIMD keep loads in flight.
+template <int G, int RB, bool PRECISE>
+__global__ __launch_bounds__(64 * kVerifyWaves, RB <= 2 ? 2 : 1) void verify_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float sm_buf[verify_smem_floats<kVerifyWaves>()];
+  decode_even_body<G, kVerifyWaves, RB, PRECISE>(p, blockIdx.x, gridDim.x, sm_buf);
+}
+
+// Row blocks built per G: q_s * G <= 16 * RB, RB in {1, 2, 4} (G = 1: q_s <= 16
+// is one block).
+template <bool PRECISE>
+const void* verify_ptr_p(int group, int rb) {
+  switch (group) {
+    case 1:
+      return rb == 1 ? reinterpret_cast<const void*>(&verify_kernel<1, 1, PRECISE>) : nullptr;
+    case 2:
+      return rb == 1   ? reinterpret_cast<const void*>(&verify_kernel<2, 1, PRECISE>)
+             : rb == 2 ? reinterpret_cast<const void*>(&verify_kernel<2, 2, PRECISE>)
+                       : nullptr;
+    case 4:
+      return rb == 1   ? reinterpret_cast<const void*>(&verify_kernel<4, 1, PRECISE>)
+             : rb == 2 ? reinterpret_cast<const void*>(&verify_kernel<4, 2, PRECISE>)
+             : rb == 4 ? reinterpret_cast<const void*>(&verify_kernel<4, 4, PRECISE>)
+                       : nullptr;
+    case 8:
+      return rb == 1   ? reinterpret_cast<const void*>(&verify_kernel<8, 1, PRECISE>)
+             : rb == 2 ? reinterpret_cast<const void*>(&verify_kernel<8, 2, PRECISE>)
+             : rb == 4 ? reinterpret_cast<const void*>(&verify_kernel<8, 4, PRECISE>)
+                       : nullptr;
+    case 16:
+      return rb == 1   ? reinterpret_cast<const void*>(&verify_kernel<16, 1, PRECISE>)
+             : rb == 2 ? reinterpret_cast<const void*>(&verify_kernel<16, 2, PRECISE>)
+             : rb == 4 ? reinterpret_cast<const void*>(&verify_kernel<16, 4, PRECISE>)
+                       : nullptr;
+    default: return nullptr;
+  }
+}
+
+const void* verify_ptr(int group, int rb, bool precise) {
+  return precise ? verify_ptr_p<true>(group, rb) : verify_ptr_p<false>(group, rb);
+}
+
+int rb_index(int rb) { return rb == 1 ? 0 : rb == 2 ? 1 : 2; }
+int group_index(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : g == 8 ? 3 : 4; }
+
+}  // namespace
+
+int verify_row_blocks(int group, int max_query_len) {
+  const int rows = group * max_query_len;
+  const int rb = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 64 ? 4 : 0;
+  return rb;
+}
+
+int verify_resident(int group, int rb, bool precise) {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs][5][3][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  std::atomic<int>& slot = cache[dev][group_index(group)][rb_index(rb)][precise ? 1 : 0];
+  const int cached = slot.load(std::memory_order_relaxed);
+  if (cached > 0) return cached;
+  const void* k = verify_ptr(group, rb, precise);
+  int cus = 0, per_cu = 0;
+  if (!k || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * kVerifyWaves, 0) != hipSuccess)
+    return 0;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  slot.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+hipError_t launch_verify(const DecodeParams& p, int group, int rb, bool precise, int nw,
+                         hipStream_t stream) {
+  const void* k = verify_ptr(group, rb, precise);
+  if (!k || nw <= 0) return hipErrorInvalidValue;
+  DecodeParams a = p;
+  void* args[] = {&a};
+  return hipLaunchKernel(k, dim3(nw), dim3(64 * kVerifyWaves), args, 0, stream);
+}
+
+}  // namespace pa

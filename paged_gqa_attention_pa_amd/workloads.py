@@ -36,9 +36,10 @@ class WorkloadSpec:
 
     context_lens / query_lens are either explicit lists or drawn: when
     ``ctx_range`` is set, ``num_draw`` context lengths are drawn uniformly in
-    [lo, hi] (inclusive) and come first in the batch, with query length 1
-    (decode); ``fixed`` lists (context_len, query_len) pairs appended after
-    them.
+    [lo, hi] (inclusive) and come first in the batch, with query length
+    ``draw_query_len`` (1: decode; a few tokens: speculative-decode
+    verification); ``fixed`` lists (context_len, query_len) pairs appended
+    after them.
     """
     name: str
     seed: int
@@ -54,13 +55,14 @@ class WorkloadSpec:
     max_blocks: Optional[int] = None   # block-table row stride; default = bound
     decode_layout: bool = False        # every query length 1 -> no query_start_loc
     logit_gain: float = 1.0            # multiplies Q after drawing (stress cases)
+    draw_query_len: int = 1            # query tokens of each drawn sequence
 
     @property
     def scale(self) -> float:
         return float(np.float32(1.0 / math.sqrt(self.head_dim)))
 
 
-# The five workloads: Llama-3.1-8B-shaped attention, bf16, page size 16.
+# The workloads: Llama-3.1-8B-shaped attention, bf16, page size 16.
 WORKLOADS = {
     # single decode step, batch 1, context 512
     "decode_ctx512": WorkloadSpec(
@@ -83,9 +85,14 @@ WORKLOADS = {
     "mixed_unified": WorkloadSpec(
         name="mixed_unified", seed=1005, pool_pages=40000, ctx_range=(512, 16384),
         num_draw=16, fixed=[(4608, 512)] * 2, max_blocks=1024),
+    # speculative-decode verification: 64 sequences, contexts U[128, 8192],
+    # 4 causal query tokens each (3 drafted + 1), one pa_prefill launch
+    "spec_verify_b64": WorkloadSpec(
+        name="spec_verify_b64", seed=1006, pool_pages=40000, ctx_range=(128, 8192),
+        num_draw=64, max_blocks=512, draw_query_len=4),
 }
 WORKLOAD_ORDER = ["decode_ctx512", "decode_ctx32k", "decode_b64",
-                  "prefill_chunk2048", "mixed_unified"]
+                  "prefill_chunk2048", "mixed_unified", "spec_verify_b64"]
 
 
 @dataclasses.dataclass
@@ -128,7 +135,7 @@ def _lengths(spec: WorkloadSpec, g: torch.Generator):
         lo, hi = spec.ctx_range
         drawn = torch.randint(lo, hi + 1, (spec.num_draw,), generator=g, device=g.device)
         ctx += [int(x) for x in drawn.cpu()]
-        ql += [1] * spec.num_draw
+        ql += [spec.draw_query_len] * spec.num_draw
     for c, q in spec.fixed:
         ctx.append(int(c))
         ql.append(int(q))

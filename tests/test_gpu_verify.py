@@ -1,0 +1,143 @@
+"""GPU parity of short query runs (speculative-decode verification) through
+pa_prefill, against the fp64 oracle.
+
+A batch whose longest query run has 2 <= q and q * G <= 64 takes the
+short-run kernel: each (sequence, kv head) unit is one Q-block of q tokens x
+G heads, streamed with the decode path's even-work grid, and units cut into
+several pieces are merged by log-sum-exp.  Tolerances are those of the other
+parity tests; the indexing cases must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_gqa_attention_pa_amd import pa, workloads
+from test_gpu_parity import _dominant_batch, _permuted, compare, dev, log, run_prefill  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+VERIFY_CASES = [
+    # (name, contexts, query lens, Hq, Hkv, causal)
+    ("q4", [5, 16, 17, 300, 1000, 4100], [4, 4, 4, 4, 4, 4], 32, 8, True),
+    ("ragged_q", [64, 2049, 33, 700, 8, 1, 16], [2, 3, 5, 8, 8, 1, 16], 32, 8, True),
+    ("q16_g4", [16, 100, 3000], [16, 16, 9], 32, 8, True),
+    ("whole_context", [2, 7, 16], [2, 7, 16], 32, 8, True),
+    ("empty_seqs", [100, 0, 50, 9], [3, 0, 2, 0], 32, 8, True),
+    ("g1_q16", [500, 17, 2000], [16, 11, 2], 8, 8, True),
+    ("g2_q16", [500, 17, 2000], [16, 11, 2], 16, 8, True),
+    ("g8_q8", [500, 17, 2000], [8, 5, 2], 64, 8, True),
+    ("g16_q4", [500, 17, 2000], [4, 3, 2], 16, 1, True),
+    ("noncausal", [300, 45, 1000], [6, 4, 8], 32, 8, False),
+    ("long_context", [40000, 300], [4, 3], 32, 8, True),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql,hq,hkv,causal", VERIFY_CASES,
+                         ids=[c[0] for c in VERIFY_CASES])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_verify_small(dev, name, ctx, ql, hq, hkv, causal, out_dtype):
+    log(f"[verify {name} {out_dtype}]")
+    spec = workloads.small_spec(f"ver_{name}", seed=800 + sum(ql) + hq, contexts=ctx, queries=ql,
+                                num_q_heads=hq, num_kv_heads=hkv, causal=causal,
+                                decode_layout=False)
+    b = workloads.generate(spec, dev)
+    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                         b.max_context_len, b.max_query_len, causal=causal)
+    tiles, _ = pa.select_tiles(pb)
+    assert tiles.q_tokens_per_tile == b.max_query_len, "not the short-run path"
+    out, lse = run_prefill(b, out_dtype)
+    compare(b, out, lse, label=f"verify {name}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 64])
+def test_verify_split_counts_stale_workspace(dev, splits):
+    """Forced split counts over a workspace of 0xFF bytes (NaN partials,
+    piece counts of -1): units cut into up to splits + 1 pieces."""
+    log(f"[verify splits={splits} stale workspace]")
+    spec = workloads.small_spec("ver_split", seed=820 + splits, contexts=[4000, 33, 2500, 16, 900],
+                                queries=[4, 2, 8, 3, 5], decode_layout=False, pool_slack=20)
+    b = workloads.generate(spec, dev)
+    for dt in (torch.bfloat16, torch.float32):
+        pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                             b.max_context_len, b.max_query_len, out_dtype=dt)
+        t, _ = pa.select_tiles(pb)
+        t.num_splits = splits
+        ws = torch.full((pa.workspace_size(pb, t),), 0xFF, dtype=torch.uint8, device=dev)
+        lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=dev)
+        out = pa.prefill(b.q, b.query_start_loc, b.k_pool, b.v_pool, b.block_tables,
+                         b.context_lens, spec.scale, b.max_context_len, b.max_query_len,
+                         out_dtype=dt, lse=lse, tiles=t, workspace=ws, problem=pb)
+        torch.cuda.synchronize()
+        compare(b, out, lse, label=f"verify S={splits} {dt}")
+
+
+def test_verify_dominant_logit_bitexact(dev):
+    log("[verify dominant logit]")
+    L, q = 300, 4
+    tstars = [0, 15, 16, 200, 296]  # all <= L - q: every row of the run sees t*
+    b = _dominant_batch(dev, tstars, L, prefill_q=q)
+    for dt in (torch.bfloat16, torch.float32):
+        out, _ = run_prefill(b, dt)
+        for s, t in enumerate(tstars):
+            page = int(b.block_tables[s, t // 16])
+            want = b.v_pool[page, t % 16].repeat_interleave(4, dim=0).to(dt)
+            got = out[s * q:(s + 1) * q]
+            ok = (torch.equal(got.view(torch.int16), want.view(torch.int16).expand_as(got))
+                  if dt == torch.bfloat16 else torch.equal(got, want.expand_as(got)))
+            assert ok, f"seq {s} t*={t} {dt}"
+
+
+def test_verify_page_permutation_and_nan_bitexact(dev):
+    log("[verify permutation / NaN poison]")
+    spec = workloads.small_spec("vperm", seed=47, contexts=[301, 77, 40, 1000], queries=[4, 7, 1, 2],
+                                pool_slack=30, decode_layout=False)
+    b = workloads.generate(spec, dev, fill="nan")
+    bz = workloads.generate(spec, dev, fill="zero")
+    o1, l1 = run_prefill(b, torch.float32)
+    o2, l2 = run_prefill(_permuted(b), torch.float32)
+    o3, l3 = run_prefill(bz, torch.float32)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_verify_rows_match_decode(dev):
+    """Row i of a causal run over L keys equals a decode step over the first
+    L - q + i + 1 keys of the same pages (fp32 outputs, both paths' own
+    rounding: agreement to the fp32 tolerance, not bits)."""
+    log("[verify rows vs decode]")
+    L, q = 3000, 6
+    spec = workloads.small_spec("vdec", seed=48, contexts=[L], queries=[q], decode_layout=False)
+    b = workloads.generate(spec, dev)
+    out, _ = run_prefill(b, torch.float32)
+    for i in range(q):
+        lens = torch.tensor([L - q + i + 1], dtype=torch.int32, device=dev)
+        o = pa.decode(b.q[i:i + 1].contiguous(), b.k_pool, b.v_pool, b.block_tables, lens,
+                      spec.scale, L - q + i + 1, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        err = float((o[0] - out[i]).abs().max())
+        assert err <= 2e-3, f"row {i}: {err}"
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 1)], ids=["g4", "g16"])
+@pytest.mark.parametrize("variant", [2, 6], ids=["static", "even"])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_prefill_single_token_batch(dev, hq, hkv, variant, splits):
+    """pa_prefill on a batch whose sequences have at most one query token
+    (one with none) runs on the decode kernels."""
+    log(f"[prefill single-token batch G={hq // hkv} variant={variant} S={splits}]")
+    spec = workloads.small_spec("pre_q1", seed=830 + hq + splits, contexts=[700, 50, 3000, 1, 16],
+                                queries=[1, 0, 1, 1, 1], num_q_heads=hq, num_kv_heads=hkv,
+                                decode_layout=False)
+    b = workloads.generate(spec, dev)
+    for dt in (torch.bfloat16, torch.float32):
+        pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                             b.max_context_len, 1, out_dtype=dt)
+        t, _ = pa.select_tiles(pb)
+        t.num_splits, t.variant = splits, variant
+        ws = torch.full((max(pa.workspace_size(pb, t), 16),), 0xFF, dtype=torch.uint8, device=dev)
+        lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=dev)
+        out = pa.prefill(b.q, b.query_start_loc, b.k_pool, b.v_pool, b.block_tables,
+                         b.context_lens, spec.scale, b.max_context_len, 1, out_dtype=dt,
+                         lse=lse, tiles=t, workspace=ws, problem=pb)
+        torch.cuda.synchronize()
+        compare(b, out, lse, label=f"single-token prefill G={hq // hkv} v{variant} S={splits} {dt}")
