@@ -46,6 +46,8 @@ PREFILL_TRAFFIC = {
     "prefill_chunk2048": 185374421,
     # unified_kernel<4,false> + splitkv_reduce_kernel (profiles/mixed_unified_kernel_trace.md)
     "mixed_unified": 643105086,
+    # verify_kernel<4,1,false> + unit_merge_kernel (profiles/spec_verify_b64_kernel_trace.md)
+    "spec_verify_b64": 1204251891,
 }
 
 # The same for one pa_cache_append call.

@@ -177,9 +177,7 @@ pa_status prefill_short_runs(const pa_problem* problem, const pa_tiles* tiles, c
   r.piece_counts = d.piece_counts;
   r.context_lens = context_lens;
   r.group = G;
-  r.token_rows = 1;
-  r.num_seqs = problem->num_seqs;
-  return from_hip(pa::launch_reduce(r, stream));
+  return from_hip(pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, stream));
 }
 
 }  // namespace
@@ -340,8 +338,6 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
     r.piece_counts = even ? p.piece_counts : nullptr;
     r.context_lens = context_lens;
     r.group = G;
-    r.token_rows = 0;
-    r.num_seqs = problem->num_seqs;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -477,8 +473,6 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
       r.piece_counts = d.piece_counts;
       r.context_lens = context_lens;
       r.group = G;
-      r.token_rows = 0;
-      r.num_seqs = problem->num_seqs;
       st = from_hip(pa::launch_reduce(r, stream));
     }
     return st;
@@ -524,8 +518,6 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     r.piece_counts = d.piece_counts;
     r.context_lens = context_lens;
     r.group = G;
-    r.token_rows = 0;
-    r.num_seqs = problem->num_seqs;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -586,8 +578,6 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
   r.piece_counts = nullptr;
   r.context_lens = nullptr;
   r.group = 1;
-  r.token_rows = 0;
-  r.num_seqs = 0;
   return from_hip(pa::launch_reduce(r, stream));
 }
 

@@ -84,11 +84,6 @@ struct ReduceParams {
   const int32_t* piece_counts;
   const int32_t* context_lens;
   int32_t group;
-  // Short query runs: rows are (token, q head) pairs of every sequence,
-  // output row = partial row; the sequence of a row (for piece_counts and
-  // context_lens) is found in query_start_loc.
-  int32_t token_rows;
-  int32_t num_seqs;
 };
 
 // Merge of split query tiles: one workgroup per (query tile, kv head) of the
@@ -130,6 +125,10 @@ hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int g
 // Workgroups of the unified prefill kernel that fit on the device at once.
 int unified_resident(int group, bool precise_p);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+// Short-run path: merge the pieces of every (sequence, kv head) unit (rows
+// are (token, q head) pairs; piece_counts, context_lens and
+// query_start_loc are required); units = num_seqs * num_kv_heads.
+hipError_t launch_unit_merge(const ReduceParams& p, int units, hipStream_t stream);
 // Short query runs (1 <= q_s, q_s * G <= 64): 16-row blocks per unit (1, 2
 // or 4; 0 when max_query_len * G exceeds 64), resident workgroups of that
 // kernel, and the even-work launch of nw workgroups.

@@ -20,6 +20,8 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPre = 4;  // partial-O loads per thread issued up front
+constexpr int kMaxUnitRows = 64;  // rows of one short-run unit (q_s * G)
 
 __device__ float block_reduce(float v, bool is_max, float* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -44,18 +46,8 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   int64_t orow = row;
-  int b = row / p.num_q_heads;  // sequence of the row
-  if (p.query_start_loc && p.token_rows) {
-    // rows are (token, head) pairs: the last sequence starting at or before
-    // the token owns it (empty sequences own no tokens)
-    const int t = row / p.num_q_heads;
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.query_start_loc[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-  } else if (p.query_start_loc) {  // mixed batch: merge the single-token sequences only
+  const int b = row / p.num_q_heads;  // sequence of the row
+  if (p.query_start_loc) {  // mixed batch: merge the single-token sequences only
     const int s = row / p.num_q_heads;
     const int q0 = p.query_start_loc[s];
     if (p.query_start_loc[s + 1] - q0 != 1) return;
@@ -83,6 +75,23 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
   }
   const float* lse_row = p.part_lse + (int64_t)row * stride;
 
+  // Up to kPre * (threads / (D/4)) splits: each thread's partial-O loads are
+  // issued here, before the weights are known, so the workgroup waits on
+  // memory once rather than twice.
+  const int items = D / 4;
+  const bool pre = items <= kThreads && S <= (kThreads / items) * kPre;
+  float4 pv[kPre];
+  if (pre) {
+    const int groups = kThreads / items, item = tid % items, grp = tid / items;
+    const float* src = p.part_o + (int64_t)row * stride * D + 4 * item;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int k = grp + u * groups;
+      pv[u] = (grp < groups && k < S) ? *reinterpret_cast<const float4*>(src + (int64_t)k * D)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
   float M = kNegInf;
   for (int k = tid; k < S; k += kThreads) {
     const float l = lse_row[k];
@@ -102,14 +111,26 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
   wsum = block_reduce(wsum, false, scratch);  // also orders the w_lds writes
   const float inv = (M != kNegInf) ? 1.f / wsum : 0.f;
 
-  const int items = D / 4;
   for (int base = 0; base < items; base += kThreads) {
     const int chunk = min(kThreads, items - base);
     const int groups = kThreads / chunk;
     const int item = base + tid % chunk;
     const int grp = tid / chunk;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (grp < groups && M != kNegInf) {
+    if (pre && grp < groups && M != kNegInf) {
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        const int k = grp + u * groups;
+        if (k < S) {
+          const float w = w_lds[k];
+          const bool on = w != 0.f;
+          o.x = fmaf(w, on ? pv[u].x : 0.f, o.x);
+          o.y = fmaf(w, on ? pv[u].y : 0.f, o.y);
+          o.z = fmaf(w, on ? pv[u].z : 0.f, o.z);
+          o.w = fmaf(w, on ? pv[u].w : 0.f, o.w);
+        }
+      }
+    } else if (grp < groups && M != kNegInf) {
       const float* src = p.part_o + (int64_t)row * stride * D + 4 * item;
       // Eight independent loads per batch; an empty split (weight 0) may hold
       // stale values, so its contribution is selected away, not multiplied.
@@ -159,6 +180,104 @@ __global__ __launch_bounds__(kThreads) void splitkv_reduce_kernel(ReduceParams p
     }
   }
   if (p.lse && tid == 0) p.lse[orow] = (M == kNegInf) ? kNegInf : M + fast_log2(wsum) * kLn2;
+}
+
+// Merge of the short-run path's pieces: one workgroup per (sequence, kv head)
+// unit, so a row's sequence is the workgroup's and no search is needed.  The
+// unit's rows r = 0 .. q_s*G-1 (token r / G, head g*G + r % G) go eight at a
+// time over the workgroup, 32 lanes per row with 4 dims each; every lane
+// reads the row's piece lse values itself (one broadcast load each) and its
+// own 16 bytes of every piece.  Units written in one piece are skipped; an
+// empty context gives O = 0, lse = -inf.
+__global__ __launch_bounds__(kThreads) void unit_merge_kernel(ReduceParams p) {
+  constexpr int kRowsPerPass = kThreads / 32;
+  const int G = p.group;
+  const int Hkv = p.num_q_heads / G;
+  const int u = blockIdx.x;
+  const int b = u / Hkv, g = u % Hkv;
+  const int q0 = p.query_start_loc[b];
+  const int qn = p.query_start_loc[b + 1] - q0;
+  const int R = qn * G;
+  if (qn <= 0 || R > kMaxUnitRows) return;
+  const int L = p.context_lens[b];
+  const int stride = p.num_splits;
+  const int count = p.piece_counts[u];  // stale for an empty context: not used then
+  const int pieces = L > 0 ? min(count, stride) : 0;
+  if (L > 0 && pieces <= 1) return;
+  const int D = p.head_dim;
+  const int item = threadIdx.x & 31;
+  for (int r = threadIdx.x >> 5; r < R; r += kRowsPerPass) {
+    const int64_t row = (int64_t)(q0 + r / G) * p.num_q_heads + g * G + r % G;
+    const float* lr = p.part_lse + row * stride;
+    const float* po = p.part_o + row * stride * D;
+    for (int d0 = 4 * item; d0 < D; d0 += 128) {
+      // the first four pieces' lse and partial loads go out together
+      float l4[4];
+      float4 v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l4[j] = j < pieces ? lr[j] : kNegInf;
+        v4[j] = j < pieces ? *reinterpret_cast<const float4*>(po + (int64_t)j * D + d0)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      float M = fmaxf(fmaxf(l4[0], l4[1]), fmaxf(l4[2], l4[3]));
+      for (int k = 4; k < pieces; ++k) M = fmaxf(M, lr[k]);
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      float wsum = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float w = (l4[j] == kNegInf) ? 0.f : fast_exp2((l4[j] - M) * kLog2e);
+          const bool on = w != 0.f;
+          wsum += w;
+          o.x = fmaf(w, on ? v4[j].x : 0.f, o.x);
+          o.y = fmaf(w, on ? v4[j].y : 0.f, o.y);
+          o.z = fmaf(w, on ? v4[j].z : 0.f, o.z);
+          o.w = fmaf(w, on ? v4[j].w : 0.f, o.w);
+        }
+        int k = 4;
+        for (; k + 4 <= pieces; k += 4) {  // four independent loads in flight
+          float4 v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[j] = *reinterpret_cast<const float4*>(po + (int64_t)(k + j) * D + d0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float l = lr[k + j];
+            const float w = (l == kNegInf) ? 0.f : fast_exp2((l - M) * kLog2e);
+            const bool on = w != 0.f;
+            wsum += w;
+            o.x = fmaf(w, on ? v[j].x : 0.f, o.x);
+            o.y = fmaf(w, on ? v[j].y : 0.f, o.y);
+            o.z = fmaf(w, on ? v[j].z : 0.f, o.z);
+            o.w = fmaf(w, on ? v[j].w : 0.f, o.w);
+          }
+        }
+        for (; k < pieces; ++k) {
+          const float4 v = *reinterpret_cast<const float4*>(po + (int64_t)k * D + d0);
+          const float l = lr[k];
+          const float w = (l == kNegInf) ? 0.f : fast_exp2((l - M) * kLog2e);
+          const bool on = w != 0.f;
+          wsum += w;
+          o.x = fmaf(w, on ? v.x : 0.f, o.x);
+          o.y = fmaf(w, on ? v.y : 0.f, o.y);
+          o.z = fmaf(w, on ? v.z : 0.f, o.z);
+          o.w = fmaf(w, on ? v.w : 0.f, o.w);
+        }
+        const float inv = 1.f / wsum;
+        o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+      }
+      const int64_t off = row * D + d0;
+      if (p.out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) = o;
+      } else {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + off) =
+            make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+      }
+      if (p.lse && d0 == 0)
+        p.lse[row] = (M == kNegInf) ? kNegInf : M + fast_log2(wsum) * kLn2;
+    }
+  }
 }
 
 // Merge of split query tiles.  Workgroup (kv head g, tile x) finds its tile
@@ -260,6 +379,12 @@ hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t strea
     case 8: hipLaunchKernelGGL(tile_merge_kernel<8>, grid, block, 0, stream, p, nx); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_unit_merge(const ReduceParams& p, int units, hipStream_t stream) {
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(unit_merge_kernel, dim3(units), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
