@@ -68,7 +68,8 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment          */
-  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, page size, G    */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim != 128, page size
+                             != 16, G not in {1, 2, 4, 8, 16, 32}            */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
   PA_ERR_HIP = 4          /* a HIP launch failed                            */
 } pa_status;
@@ -144,7 +145,11 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
  * leaves the counters zero again, so it can be reused (and captured) without
  * clearing.  Calls that share one workspace must not run concurrently.
  * tiles->waves_per_wg is 4 or 8 (4 when G = 16).  Pointers to bf16 data must
- * be 16-byte aligned. */
+ * be 16-byte aligned.  problem->max_query_len must be 0 or 1.
+ * G = 32 (the decode kernels hold at most 16 query heads per KV head) runs
+ * on the short-run kernel described at pa_prefill: one token of 32 heads is
+ * a 32-row Q-block, the even-work grid always applies (waves_per_wg and the
+ * merge bits are ignored) and the workspace is always needed. */
 pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void* q,
                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
                     const int32_t* context_lens, void* out, float* lse, void* workspace,
@@ -163,14 +168,26 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
  * also holds split-KV decode workgroups for every (sequence, kv head,
  * split), which return at once for sequences whose query length is not 1.
  * Their partials are merged by a second kernel when tiles->num_splits > 1.
- * With G = 16 single-token sequences take the tile path.
+ * With G = 16 or 32 single-token sequences take the tile path.
+ * The host picks the kernels from the problem's bounds alone:
+ *   - max_query_len <= 1 (G <= 16): the decode kernels, with query_start_loc
+ *     mapping the rows (sequences with no query token are skipped);
+ *   - short query runs, 2 <= max_query_len and max_query_len * G <= 64
+ *     (speculative-decode verification, [IBM-PA] model-feature list), and
+ *     max_query_len <= 1 at G = 32: every (sequence, kv head) unit is one
+ *     Q-block of q_len(s) tokens x G heads, streamed over the decode path's
+ *     even-work grid (tiles->num_splits bounds the pieces of a unit, S + 1
+ *     partial slots per (token, head) row; waves_per_wg, q_tokens_per_tile
+ *     and tile_splits are ignored), and a second kernel merges the units cut
+ *     into several pieces;
+ *   - otherwise the query-tile launch described above.
  * q: bf16 [T, Hq, D]; out: [T, Hq, D] of out_dtype; lse: fp32 [T, Hq] or NULL.
  * With tiles->tile_splits > 1 every query tile's keys are split as well and
  * its partials ([T * Hq, tile_splits, D] fp32 plus lse) are merged by a
  * further kernel.
  * workspace: >= pa_workspace_size bytes (decode-row partials for
- * num_seqs * Hq rows, tile partials for T * Hq rows), zero-filled before
- * first use, as for pa_decode. */
+ * num_seqs * Hq rows, tile partials for T * Hq rows, or short-run partials
+ * for T * Hq rows), zero-filled before first use, as for pa_decode. */
 pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const void* q,
                      const int32_t* query_start_loc, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, const int32_t* context_lens, void* out,

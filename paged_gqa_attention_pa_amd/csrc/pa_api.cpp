@@ -19,7 +19,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-bool group_built(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+bool group_built(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32; }
 
 // Checks shared by every call; returns PA_OK or the first failure.
 pa_status check_problem(const pa_problem* pb) {
@@ -73,10 +73,20 @@ struct Workspace {
 
 // Short query runs (speculative-decode verification): every sequence of the
 // batch has at most max_query_len >= 2 tokens and max_query_len * G <= 64,
-// so a (sequence, kv head) unit is one Q-block of at most 64 rows.
+// so a (sequence, kv head) unit is one Q-block of at most 64 rows.  Decode
+// at G = 32 (32 query heads on one KV head) runs the same way: the decode
+// kernels hold at most 16 heads per KV head.
 bool verify_path(const pa_problem* pb) {
   const int G = pb->num_q_heads / pb->num_kv_heads;
+  if (G == 32 && pb->max_query_len <= 1) return true;
   return pb->max_query_len >= 2 && pa::verify_row_blocks(G, pb->max_query_len) > 0;
+}
+
+// Rows of the short-run partials: (token, q head) pairs; a decode-layout
+// problem has one token per sequence.
+int64_t short_run_rows(const pa_problem* pb) {
+  const int64_t tokens = pb->max_query_len <= 1 ? pb->num_seqs : pb->total_query_tokens;
+  return tokens * pb->num_q_heads;
 }
 
 bool even_grid(const pa_tiles* t) {
@@ -90,8 +100,7 @@ Workspace workspace_layout(const pa_problem* pb, const pa_tiles* t) {
   const bool verify = verify_path(pb);
   if (S > 1 || verify) {
     // short query runs: (token, head) rows, always the even-work grid
-    const int64_t rows = (int64_t)(verify ? pb->total_query_tokens : pb->num_seqs) *
-                         pb->num_q_heads;
+    const int64_t rows = verify ? short_run_rows(pb) : (int64_t)pb->num_seqs * pb->num_q_heads;
     const int64_t slots = S + ((verify || even_grid(t)) ? 1 : 0);
     const size_t units = (size_t)((int64_t)pb->num_seqs * pb->num_kv_heads);
     w.lse_off = align_up((size_t)(rows * slots * D) * sizeof(float));
@@ -119,17 +128,18 @@ bool may_hold_decode_rows(const pa_problem* pb) {
          (int64_t)pb->total_query_tokens < (int64_t)pb->num_seqs * pb->max_query_len;
 }
 
-// pa_prefill for short query runs: the even-work grid over every
-// (sequence, kv head) unit with one Q-block per unit, then the merge of the
-// units cut into several pieces.  Arguments were checked by the caller.
-pa_status prefill_short_runs(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+// pa_prefill for short query runs, and pa_decode at G = 32
+// (query_start_loc null): the even-work grid over every (sequence, kv head)
+// unit with one Q-block per unit, then the merge of the units cut into
+// several pieces.  Arguments were checked by the caller.
+pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const void* q,
                              const int32_t* query_start_loc, const void* k_pool,
                              const void* v_pool, const int32_t* block_tables,
                              const int32_t* context_lens, void* out, float* lse, char* ws,
                              const Workspace& wl, hipStream_t stream) {
   const int G = problem->num_q_heads / problem->num_kv_heads;
   const int S = tiles->num_splits;
-  const int rb = pa::verify_row_blocks(G, problem->max_query_len);
+  const int rb = pa::verify_row_blocks(G, problem->max_query_len > 1 ? problem->max_query_len : 1);
   const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
   pa::DecodeParams d;
   d.q = static_cast<const uint16_t*>(q);
@@ -214,7 +224,7 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
   memset(&t, 0, sizeof t);
   const pa::DecodeChoice dc = pa::table_decode(problem->num_seqs, problem->num_kv_heads,
                                                problem->max_context_len, G);
-  if (problem->max_query_len <= 1) {
+  if (problem->max_query_len <= 1 && !verify_path(problem)) {
     t.kv_tile = pa::kDecodeTile;
     t.waves_per_wg = dc.waves;
     t.q_tokens_per_tile = 1;
@@ -225,7 +235,7 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     // max_query_len tokens x G heads, 4 wavefronts, even-work grid
     t.kv_tile = pa::kDecodeTile;
     t.waves_per_wg = 4;
-    t.q_tokens_per_tile = problem->max_query_len;
+    t.q_tokens_per_tile = problem->max_query_len > 1 ? problem->max_query_len : 1;
     t.num_splits = dc.splits;
     t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
                 pa::kVariantSeparateMerge | pa::kVariantEvenWork;
@@ -266,6 +276,7 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
     return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PA_ERR_INVALID_ARG;
+  if (problem->max_query_len > 1) return PA_ERR_INVALID_ARG;  // one token per sequence
   const int S = tiles->num_splits;
   const int G = problem->num_q_heads / problem->num_kv_heads;
   const int waves = tiles->waves_per_wg;
@@ -279,6 +290,9 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
                            (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0) return PA_OK;
+  if (verify_path(problem))  // G = 32
+    return short_runs(problem, tiles, q, nullptr, k_pool, v_pool, block_tables, context_lens, out,
+                      lse, static_cast<char*>(workspace), wl, stream);
 
   const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
   pa::DecodeParams p;
@@ -370,8 +384,8 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0 || problem->total_query_tokens == 0) return PA_OK;
   if (verify_path(problem))
-    return prefill_short_runs(problem, tiles, q, query_start_loc, k_pool, v_pool, block_tables,
-                              context_lens, out, lse, static_cast<char*>(workspace), wl, stream);
+    return short_runs(problem, tiles, q, query_start_loc, k_pool, v_pool, block_tables,
+                      context_lens, out, lse, static_cast<char*>(workspace), wl, stream);
   const int qt = 256 / G;
   const float scale_log2 = problem->scale * pa::kLog2eHost;
   const int out_f32 = problem->out_dtype == PA_FP32;

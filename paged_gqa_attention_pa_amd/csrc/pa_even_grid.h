@@ -36,7 +36,7 @@ __device__ void decode_even_body(const DecodeParams& p, int w, int nw, float* sm
     if constexpr (RB == 0) {
       if (p.query_start_loc && p.query_start_loc[b + 1] - p.query_start_loc[b] != 1) return 0;
     } else {
-      const int qn = p.query_start_loc[b + 1] - p.query_start_loc[b];
+      const int qn = p.query_start_loc ? p.query_start_loc[b + 1] - p.query_start_loc[b] : 1;
       if (qn <= 0 || qn * G > 16 * RB) return 0;
     }
     const int L = p.context_lens[b];

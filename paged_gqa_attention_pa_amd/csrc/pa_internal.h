@@ -126,8 +126,9 @@ hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int g
 int unified_resident(int group, bool precise_p);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 // Short-run path: merge the pieces of every (sequence, kv head) unit (rows
-// are (token, q head) pairs; piece_counts, context_lens and
-// query_start_loc are required); units = num_seqs * num_kv_heads.
+// are (token, q head) pairs; piece_counts and context_lens are required,
+// query_start_loc null means one token per sequence); units = num_seqs *
+// num_kv_heads.
 hipError_t launch_unit_merge(const ReduceParams& p, int units, hipStream_t stream);
 // Short query runs (1 <= q_s, q_s * G <= 64): 16-row blocks per unit (1, 2
 // or 4; 0 when max_query_len * G exceeds 64), resident workgroups of that

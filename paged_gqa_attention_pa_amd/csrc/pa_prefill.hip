@@ -77,6 +77,10 @@ hipError_t launch_t(const PrefillParams& pp, const DecodeParams& dp, int group, 
       if (n_dec != 0) return hipErrorInvalidValue;
       hipLaunchKernelGGL((unified_kernel<16, PRECISE>), grid, block, 0, stream, pp, dp, nx);
       break;
+    case 32:
+      if (n_dec != 0) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((unified_kernel<32, PRECISE>), grid, block, 0, stream, pp, dp, nx);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -90,6 +94,7 @@ const void* unified_ptr(int group) {
     case 4: return reinterpret_cast<const void*>(&unified_kernel<4, PRECISE>);
     case 8: return reinterpret_cast<const void*>(&unified_kernel<8, PRECISE>);
     case 16: return reinterpret_cast<const void*>(&unified_kernel<16, PRECISE>);
+    case 32: return reinterpret_cast<const void*>(&unified_kernel<32, PRECISE>);
     default: return nullptr;
   }
 }
@@ -98,10 +103,10 @@ const void* unified_ptr(int group) {
 
 int unified_resident(int group, bool precise_p) {
   constexpr int kDevs = 64;
-  static std::atomic<int> cache[kDevs][5][2];
+  static std::atomic<int> cache[kDevs][6][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
-  const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
+  const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : group == 16 ? 4 : 5;
   const int cached = cache[dev][gi][precise_p].load(std::memory_order_relaxed);
   if (cached > 0) return cached;
   const void* k = precise_p ? unified_ptr<true>(group) : unified_ptr<false>(group);

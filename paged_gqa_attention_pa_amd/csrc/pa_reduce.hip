@@ -195,8 +195,9 @@ __global__ __launch_bounds__(kThreads) void unit_merge_kernel(ReduceParams p) {
   const int Hkv = p.num_q_heads / G;
   const int u = blockIdx.x;
   const int b = u / Hkv, g = u % Hkv;
-  const int q0 = p.query_start_loc[b];
-  const int qn = p.query_start_loc[b + 1] - q0;
+  // query_start_loc null: sequence b owns token b (decode layout)
+  const int q0 = p.query_start_loc ? p.query_start_loc[b] : b;
+  const int qn = p.query_start_loc ? p.query_start_loc[b + 1] - q0 : 1;
   const int R = qn * G;
   if (qn <= 0 || R > kMaxUnitRows) return;
   const int L = p.context_lens[b];

@@ -1,5 +1,6 @@
 // Short-query-run kernels for gfx950 (speculative-decode verification
-// batches: every sequence has 1 <= q_s query tokens with q_s * G <= 64): the
+// batches: every sequence has 1 <= q_s query tokens with q_s * G <= 64; also
+// decode at G = 32, one token of 32 heads being two 16-row blocks): the
 // even-work grid of the decode path driving verify_body (pa_verify_body.h),
 // one instantiation per (G, row blocks RB, precise P).  Rows are
 // (token, q head) pairs: partials are [T*Hq, slots, D].
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, RB <= 2 ? 2 : 1) void verify_ker
 }
 
 // Row blocks built per G: q_s * G <= 16 * RB, RB in {1, 2, 4} (G = 1: q_s <= 16
-// is one block).
+// is one block; G = 32: one or two tokens, two or four blocks).
 template <bool PRECISE>
 const void* verify_ptr_p(int group, int rb) {
   switch (group) {
@@ -50,6 +51,10 @@ const void* verify_ptr_p(int group, int rb) {
              : rb == 2 ? reinterpret_cast<const void*>(&verify_kernel<16, 2, PRECISE>)
              : rb == 4 ? reinterpret_cast<const void*>(&verify_kernel<16, 4, PRECISE>)
                        : nullptr;
+    case 32:
+      return rb == 2   ? reinterpret_cast<const void*>(&verify_kernel<32, 2, PRECISE>)
+             : rb == 4 ? reinterpret_cast<const void*>(&verify_kernel<32, 4, PRECISE>)
+                       : nullptr;
     default: return nullptr;
   }
 }
@@ -59,7 +64,9 @@ const void* verify_ptr(int group, int rb, bool precise) {
 }
 
 int rb_index(int rb) { return rb == 1 ? 0 : rb == 2 ? 1 : 2; }
-int group_index(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : g == 8 ? 3 : 4; }
+int group_index(int g) {
+  return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : g == 8 ? 3 : g == 16 ? 4 : 5;
+}
 
 }  // namespace
 
@@ -71,7 +78,7 @@ int verify_row_blocks(int group, int max_query_len) {
 
 int verify_resident(int group, int rb, bool precise) {
   constexpr int kDevs = 64;
-  static std::atomic<int> cache[kDevs][5][3][2];
+  static std::atomic<int> cache[kDevs][6][3][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
   std::atomic<int>& slot = cache[dev][group_index(group)][rb_index(rb)][precise ? 1 : 0];

@@ -65,8 +65,9 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   const int lane = tid & 63;
   const int c = lane >> 4;
   const int n = lane & 15;
-  const int q0 = p.query_start_loc[b];
-  const int qn = p.query_start_loc[b + 1] - q0;
+  // query_start_loc null: sequence b owns token b (decode layout)
+  const int q0 = p.query_start_loc ? p.query_start_loc[b] : b;
+  const int qn = p.query_start_loc ? p.query_start_loc[b + 1] - q0 : 1;
   const int R = qn * G;
   if (qn <= 0 || R > 16 * RB) return;  // no rows, or above the host bound
 

@@ -92,11 +92,39 @@ def test_select_tiles_decode_and_prefill(lib):
     ("scale", 0.0, pa.PA_ERR_INVALID_ARG),
     ("scale", -0.5, pa.PA_ERR_INVALID_ARG),
     ("scale", float("inf"), pa.PA_ERR_INVALID_ARG),
-    ("num_kv_heads", 1, pa.PA_ERR_UNSUPPORTED),       # G = 32 not built
 ])
 def test_select_tiles_rejects(lib, field, value, status):
     st, _, _ = _select(lib, _problem(**{field: value}))
     assert st == status
+
+
+def test_group_sizes_built(lib):
+    for hq, hkv in [(8, 8), (16, 8), (32, 8), (64, 8), (16, 1), (32, 1)]:
+        st, t, _ = _select(lib, _problem(num_q_heads=hq, num_kv_heads=hkv))
+        assert st == pa.PA_OK, (hq, hkv)
+    st, _, _ = _select(lib, _problem(num_q_heads=64, num_kv_heads=1))  # G = 64
+    assert st == pa.PA_ERR_UNSUPPORTED
+
+
+def test_select_tiles_short_runs(lib):
+    """Short query runs (2 <= max_query_len, max_query_len * G <= 64) and
+    decode at G = 32 take one Q-block per (sequence, kv head) unit on the
+    even-work grid, with a workspace of S + 1 slots per (token, head) row."""
+    cases = [dict(max_query_len=4, total_query_tokens=16),           # G = 4, 16 rows
+             dict(max_query_len=16, total_query_tokens=64),          # G = 4, 64 rows
+             dict(num_q_heads=32, num_kv_heads=1, max_query_len=1),  # G = 32 decode
+             dict(num_q_heads=32, num_kv_heads=1, max_query_len=2, total_query_tokens=8)]
+    for kw in cases:
+        pb = _problem(**kw)
+        st, t, ws = _select(lib, pb)
+        assert st == pa.PA_OK, kw
+        assert t.kv_tile == 16 and t.waves_per_wg == 4 and (t.variant & 6) == 6, kw
+        rows = pb.total_query_tokens * pb.num_q_heads if pb.max_query_len > 1 \
+            else pb.num_seqs * pb.num_q_heads
+        assert ws >= rows * (t.num_splits + 1) * 129 * 4, kw
+    # 17 tokens x 4 heads = 68 rows: the query tiles
+    st, t, _ = _select(lib, _problem(max_query_len=17, total_query_tokens=68))
+    assert st == pa.PA_OK and t.kv_tile == 32
 
 
 @pytest.mark.parametrize("ts", [-1, 9])
@@ -137,6 +165,10 @@ def test_compute_calls_reject_before_launch(lib):
     t4 = pa.Tiles(32, 1, 8, 64, 0, 2)
     assert lib.pa_prefill(ctypes.byref(pt), ctypes.byref(t4), fake, fake, fake, fake, fake, fake,
                           fake, nul, nul, 0, nul) == pa.PA_ERR_WORKSPACE
+    # a decode call given a problem with longer query runs
+    pq = _problem(max_query_len=4, total_query_tokens=16)
+    assert lib.pa_decode(ctypes.byref(pq), ctypes.byref(t), fake, fake, fake, fake, fake, fake,
+                         nul, nul, 0, nul) == pa.PA_ERR_INVALID_ARG
     # prefill without query_start_loc
     pp = _problem(max_query_len=64, total_query_tokens=256)
     assert lib.pa_prefill(ctypes.byref(pp), ctypes.byref(t), fake, nul, fake, fake, fake, fake,

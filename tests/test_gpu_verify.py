@@ -12,7 +12,8 @@ import pytest
 import torch
 
 from paged_gqa_attention_pa_amd import pa, workloads
-from test_gpu_parity import _dominant_batch, _permuted, compare, dev, log, run_prefill  # noqa: F401
+from test_gpu_parity import (_dominant_batch, _permuted, compare, dev, log,  # noqa: F401
+                             run_decode, run_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -141,3 +142,43 @@ def test_prefill_single_token_batch(dev, hq, hkv, variant, splits):
                          lse=lse, tiles=t, workspace=ws, problem=pb)
         torch.cuda.synchronize()
         compare(b, out, lse, label=f"single-token prefill G={hq // hkv} v{variant} S={splits} {dt}")
+
+
+# ---------------------------------------------------- 32 heads per KV head ----
+
+G32_DECODE = [1, 15, 16, 17, 300, 1000, 0, 2049]
+
+
+@pytest.mark.parametrize("splits", [None, 1, 3, 64])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_g32_decode(dev, splits, out_dtype):
+    """pa_decode with 32 query heads on one KV head: one token of 32 heads is
+    two 16-row blocks of the short-run kernel (decode layout, no
+    query_start_loc)."""
+    log(f"[decode G=32 S={splits} {out_dtype}]")
+    spec = workloads.small_spec("g32_dec", seed=850, contexts=G32_DECODE,
+                                queries=[1] * len(G32_DECODE), num_q_heads=32, num_kv_heads=1)
+    b = workloads.generate(spec, dev)
+    out, lse = run_decode(b, out_dtype, splits)
+    compare(b, out, lse, label=f"decode G=32 S={splits}")
+
+
+G32_PREFILL = [
+    # (name, contexts, query lens): one-token rows, two-token runs (the
+    # short-run kernel), chunks (query tiles of 8 tokens x 32 heads), a mix
+    ("q1", [700, 50, 3000, 1, 16], [1, 0, 1, 1, 1]),
+    ("q2", [700, 50, 3000, 2, 16], [2, 1, 2, 2, 1]),
+    ("chunks", [300, 77, 1000], [140, 77, 31]),
+    ("mixed", [900, 40, 260, 513], [1, 1, 100, 200]),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql", G32_PREFILL, ids=[c[0] for c in G32_PREFILL])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_g32_prefill(dev, name, ctx, ql, out_dtype):
+    log(f"[prefill G=32 {name} {out_dtype}]")
+    spec = workloads.small_spec(f"g32_{name}", seed=860 + sum(ql), contexts=ctx, queries=ql,
+                                num_q_heads=32, num_kv_heads=1, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    out, lse = run_prefill(b, out_dtype)
+    compare(b, out, lse, label=f"prefill G=32 {name}")
