@@ -68,8 +68,11 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment          */
-  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim != 128, page size
-                             != 16, G not in {1, 2, 4, 8, 16, 32}            */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128/256,
+                             page size != 16, G not in {1,2,4,8,16,32}, and
+                             at head_dim 64/256 query runs beyond the
+                             short-run kernel (max_query_len * G > 64, > 32
+                             at 256)                                        */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
   PA_ERR_HIP = 4          /* a HIP launch failed                            */
 } pa_status;
@@ -81,7 +84,7 @@ typedef struct pa_problem {
   int32_t num_seqs;           /* B >= 0                                         */
   int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads                 */
   int32_t num_kv_heads;       /* Hkv                                            */
-  int32_t head_dim;           /* D; 128 is built                                */
+  int32_t head_dim;           /* D: 64, 128 or 256 (see PA_ERR_UNSUPPORTED)     */
   int32_t page_size;          /* P; 16 is built                                 */
   int32_t max_blocks_per_seq; /* row stride of block_tables                     */
   int64_t kv_stride_page;     /* pool strides in elements, multiples of 8       */

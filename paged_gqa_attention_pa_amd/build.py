@@ -4,10 +4,12 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -26,30 +28,54 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def command(out: str):
-    return ([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-             # packed fp32 VALU ops stay off on this target
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-I", os.path.join(ROOT, "include"), "-o", out]
-            + [os.path.join(CSRC, s) for s in SOURCES])
+FLAGS = ["-O3", "-std=c++17", "-fPIC",
+         # packed fp32 VALU ops stay off on this target
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+NOISE = "packed-fp32-ops"  # the host pass warns that it does not know the feature
+
+
+def compile_command(src: str, obj: str):
+    return ([hipcc(), f"--offload-arch={ARCH}"] + FLAGS +
+            ["-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj])
+
+
+def link_command(objs, out: str):
+    return [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", out] + list(objs)
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    msg = "\n".join(l for l in res.stdout.splitlines() if NOISE not in l)
+    return res.returncode, msg
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libpa.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    noise = "packed-fp32-ops"  # the host pass warns that it does not know the feature
-    msg = "\n".join(l for l in res.stdout.splitlines() if noise not in l)
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed:\n" + msg)
-    if verbose and msg.strip():
-        print(msg)
-    os.replace(tmp, LIB)
+    """Compile every source (in parallel, one object each) and link libpa.so
+    (always recompiles)."""
+    tmpdir = tempfile.mkdtemp(prefix="pa_build_")
+    try:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [compile_command(s, o) for s, o in zip(SOURCES, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        workers = max(1, min(len(cmds), os.cpu_count() or 1))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(_run, cmds))
+        for (rc, msg), src in zip(results, SOURCES):
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n" + msg)
+            if verbose and msg.strip():
+                print(msg)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        rc, msg = _run(link_command(objs, tmp))
+        if rc != 0:
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise RuntimeError("link failed:\n" + msg)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

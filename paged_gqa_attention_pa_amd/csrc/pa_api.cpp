@@ -38,7 +38,9 @@ pa_status check_problem(const pa_problem* pb) {
   if (!(pb->scale > 0.f) || pb->scale == __builtin_inff()) return PA_ERR_INVALID_ARG;
   if ((int64_t)pb->max_context_len > (int64_t)pb->max_blocks_per_seq * pb->page_size)
     return PA_ERR_INVALID_ARG;
-  if (pb->head_dim != kHeadDim || pb->page_size != kPage) return PA_ERR_UNSUPPORTED;
+  if ((pb->head_dim != 64 && pb->head_dim != kHeadDim && pb->head_dim != 256) ||
+      pb->page_size != kPage)
+    return PA_ERR_UNSUPPORTED;
   // the kernels form page offsets as 32-bit byte strides times page ids
   if (pb->kv_stride_page > 0x7fffffff || pb->kv_stride_token > 0x7fffffff ||
       pb->kv_stride_head > 0x7fffffff)
@@ -74,12 +76,23 @@ struct Workspace {
 // Short query runs (speculative-decode verification): every sequence of the
 // batch has at most max_query_len >= 2 tokens and max_query_len * G <= 64,
 // so a (sequence, kv head) unit is one Q-block of at most 64 rows.  Decode
-// at G = 32 (32 query heads on one KV head) runs the same way: the decode
-// kernels hold at most 16 heads per KV head.
+// at G = 32 (32 query heads on one KV head) runs the same way, the decode
+// kernels holding at most 16 heads per KV head, and so does decode at head
+// dims other than 128.
 bool verify_path(const pa_problem* pb) {
   const int G = pb->num_q_heads / pb->num_kv_heads;
-  if (G == 32 && pb->max_query_len <= 1) return true;
-  return pb->max_query_len >= 2 && pa::verify_row_blocks(G, pb->max_query_len) > 0;
+  if ((G == 32 || pb->head_dim != kHeadDim) && pb->max_query_len <= 1)
+    return pa::verify_row_blocks(G, 1, pb->head_dim) > 0;
+  return pb->max_query_len >= 2 && pa::verify_row_blocks(G, pb->max_query_len, pb->head_dim) > 0;
+}
+
+// Head dims other than 128 are built for decode and short query runs only
+// (the query-tile kernel is laid out for 128).
+pa_status check_attention(const pa_problem* pb) {
+  pa_status st = check_problem(pb);
+  if (st != PA_OK) return st;
+  if (pb->head_dim != kHeadDim && !verify_path(pb)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
 }
 
 // Rows of the short-run partials: (token, q head) pairs; a decode-layout
@@ -139,7 +152,8 @@ pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const voi
                              const Workspace& wl, hipStream_t stream) {
   const int G = problem->num_q_heads / problem->num_kv_heads;
   const int S = tiles->num_splits;
-  const int rb = pa::verify_row_blocks(G, problem->max_query_len > 1 ? problem->max_query_len : 1);
+  const int rb = pa::verify_row_blocks(G, problem->max_query_len > 1 ? problem->max_query_len : 1,
+                                       problem->head_dim);
   const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
   pa::DecodeParams d;
   d.q = static_cast<const uint16_t*>(q);
@@ -169,9 +183,9 @@ pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.scale_log2 = problem->scale * pa::kLog2eHost;
   d.out_f32 = problem->out_dtype == PA_FP32;
   d.causal = problem->causal;
-  const int nw = pa::verify_resident(G, rb, precise);
+  const int nw = pa::verify_resident(G, rb, precise, problem->head_dim);
   if (nw <= 0) return PA_ERR_HIP;
-  pa_status st = from_hip(pa::launch_verify(d, G, rb, precise, nw, stream));
+  pa_status st = from_hip(pa::launch_verify(d, G, rb, precise, problem->head_dim, nw, stream));
   if (st != PA_OK) return st;
   pa::ReduceParams r;
   r.part_o = d.part_o;
@@ -207,7 +221,7 @@ const char* pa_status_string(pa_status status) {
 
 pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
                             size_t* workspace_bytes) {
-  pa_status st = check_problem(problem);
+  pa_status st = check_attention(problem);
   if (st != PA_OK) return st;
   if ((st = check_tiles(tiles)) != PA_OK) return st;
   if (!workspace_bytes) return PA_ERR_INVALID_ARG;
@@ -216,7 +230,7 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
 }
 
 pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* workspace_bytes) {
-  pa_status st = check_problem(problem);
+  pa_status st = check_attention(problem);
   if (st != PA_OK) return st;
   if (!out || !workspace_bytes) return PA_ERR_INVALID_ARG;
   const int G = problem->num_q_heads / problem->num_kv_heads;
@@ -269,7 +283,7 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
                     const int32_t* context_lens, void* out, float* lse, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  pa_status st = check_problem(problem);
+  pa_status st = check_attention(problem);
   if (st != PA_OK) return st;
   if ((st = check_tiles(tiles)) != PA_OK) return st;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
@@ -362,7 +376,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
                      const int32_t* block_tables, const int32_t* context_lens, void* out,
                      float* lse, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
-  pa_status st = check_problem(problem);
+  pa_status st = check_attention(problem);
   if (st != PA_OK) return st;
   if ((st = check_tiles(tiles)) != PA_OK) return st;
   const int G = problem->num_q_heads / problem->num_kv_heads;
@@ -565,6 +579,7 @@ pa_status pa_cache_append(const pa_problem* problem, const void* k_new, const vo
   p.num_kv_heads = problem->num_kv_heads;
   p.max_blocks = problem->max_blocks_per_seq;
   p.total_tokens = problem->total_query_tokens;
+  p.head_dim = problem->head_dim;
   return from_hip(pa::launch_append(p, stream));
 }
 

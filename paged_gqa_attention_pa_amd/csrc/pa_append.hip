@@ -2,10 +2,10 @@
 //
 // Token i of sequence s lands at logical position p = L_s - q_s + i (the
 // newest q_s positions of the context, the positions pa_prefill's queries
-// hold): page block_tables[s][p / P], slot p % P.  Sixteen threads move one
-// (token, kv head) row of 256 bytes for K and for V, 16 bytes each, so a
-// wavefront reads four whole rows of the token-major input and writes four
-// whole 256-byte head slices of the pools.  A token's sequence comes from a
+// hold): page block_tables[s][p / P], slot p % P.  D / 8 threads move one
+// (token, kv head) row of 2D bytes for K and for V, 16 bytes each, so a
+// wavefront reads 512 / D whole rows of the token-major input and writes as
+// many whole head slices of the pools (four at D = 128).  A token's sequence comes from a
 // binary search of query_start_loc (sequence s owns rows
 // [qsl[s], qsl[s+1])); without it, row t is sequence t's single token.
 // The pool writes are nontemporal: nothing in this kernel reads them again,
@@ -23,8 +23,8 @@ constexpr int kAppendThreads = 256;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
-  constexpr int D = kHeadDim;
-  constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  const int D = p.head_dim;
+  const int kChunks = D / 8;  // 16-byte chunks per row
   const int64_t gid = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
   const int64_t rows = (int64_t)p.total_tokens * p.num_kv_heads;
   if (gid >= rows * kChunks) return;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  const int64_t chunks = (int64_t)p.total_tokens * p.num_kv_heads * (kHeadDim / 8);
+  const int64_t chunks = (int64_t)p.total_tokens * p.num_kv_heads * (p.head_dim / 8);
   if (chunks == 0) return hipSuccess;
   const int64_t grid = (chunks + kAppendThreads - 1) / kAppendThreads;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;

@@ -24,7 +24,7 @@ namespace decode_detail {
 // RB = 0: units of single-token sequences, decode_body.  RB >= 1: units of
 // sequences with 1 <= q_s and q_s * G <= 16 * RB query tokens, verify_body
 // (every unit is then a row block of the short-run Q-block).
-template <int G, int W, int RB = 0, bool PRECISE = false>
+template <int G, int W, int RB = 0, bool PRECISE = false, int D = kHeadDim>
 __device__ void decode_even_body(const DecodeParams& p, int w, int nw, float* sm_buf) {
   constexpr int kT = 64 * W;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -109,7 +109,7 @@ __device__ void decode_even_body(const DecodeParams& p, int w, int nw, float* sm
     if constexpr (RB == 0)
       decode_body<G, W, false, true>(p, 0, g, b, sm_buf, piece);
     else
-      verify_detail::verify_body<G, RB, W, PRECISE>(p, g, b, sm_buf, piece);
+      verify_detail::verify_body<G, RB, W, PRECISE, D>(p, g, b, sm_buf, piece);
     if (tid == 0 && w == w_last) p.piece_counts[(int64_t)b * Hkv + g] = pieces;
     __syncthreads();  // the next piece reuses the LDS merge buffers
     pos += take;

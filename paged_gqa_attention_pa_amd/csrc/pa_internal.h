@@ -108,6 +108,7 @@ struct AppendParams {
   uint16_t* v_pool;
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_kv_heads, max_blocks, total_tokens;
+  int32_t head_dim;         // 64, 128 or 256
 };
 
 // Launchers: return hipSuccess or the launch error.  Shapes were checked.
@@ -130,13 +131,13 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 // query_start_loc null means one token per sequence); units = num_seqs *
 // num_kv_heads.
 hipError_t launch_unit_merge(const ReduceParams& p, int units, hipStream_t stream);
-// Short query runs (1 <= q_s, q_s * G <= 64): 16-row blocks per unit (1, 2
-// or 4; 0 when max_query_len * G exceeds 64), resident workgroups of that
+// Short query runs (1 <= q_s, q_s * G <= 64; <= 32 at head dim 256): 16-row
+// blocks per unit (1, 2 or 4; 0 when not built), resident workgroups of that
 // kernel, and the even-work launch of nw workgroups.
-int verify_row_blocks(int group, int max_query_len);
-int verify_resident(int group, int rb, bool precise_p);
-hipError_t launch_verify(const DecodeParams& p, int group, int rb, bool precise_p, int nw,
-                         hipStream_t stream);
+int verify_row_blocks(int group, int max_query_len, int head_dim);
+int verify_resident(int group, int rb, bool precise_p, int head_dim);
+hipError_t launch_verify(const DecodeParams& p, int group, int rb, bool precise_p, int head_dim,
+                         int nw, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream);
 

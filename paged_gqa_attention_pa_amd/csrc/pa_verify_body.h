@@ -36,14 +36,19 @@ using decode_detail::EvenPiece;
 using decode_detail::kLazyThreshold;
 using decode_detail::readlane;
 
-constexpr int kVRow = 144;  // bf16 per V row in LDS: 256 B of data + 32 B pad
+// bf16 per V row in LDS: D of data + 16 of pad (the transposing reads of
+// 16 rows then fall on two bank rounds)
+template <int D>
+constexpr int v_row() {
+  return D + 16;
+}
 
 // LDS floats verify_body needs from its caller: one V tile per wavefront
 // during the loop, then one 16-column block of O per wavefront for the merge.
-template <int W>
+template <int W, int D>
 constexpr int verify_smem_floats() {
-  constexpr int vtiles = W * 16 * kVRow / 2;
-  constexpr int merge = W * 16 * kHeadDim;
+  constexpr int vtiles = W * 16 * v_row<D>() / 2;
+  constexpr int merge = W * 16 * D;
   return vtiles > merge ? vtiles : merge;
 }
 
@@ -53,13 +58,20 @@ __device__ __forceinline__ int64_t unit_row(const DecodeParams& p, int q0, int g
   return (int64_t)(q0 + r / G) * p.num_q_heads + g * G + r % G;
 }
 
-// One workgroup of W wavefronts: the piece ev of unit (sequence b, kv head g).
-// sm_buf: verify_smem_floats<W>() floats of LDS, 16-byte aligned.
-template <int G, int RB, int W, bool PRECISE>
+// One workgroup of W wavefronts: the piece ev of unit (sequence b, kv head g),
+// head dimension D (64, 128 or 256).
+// sm_buf: verify_smem_floats<W, D>() floats of LDS, 16-byte aligned.
+template <int G, int RB, int W, bool PRECISE, int D = kHeadDim>
 __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b, float* sm_buf,
                                             EvenPiece ev) {
-  constexpr int DEPTH = RB >= 2 ? 2 : 3;  // tiles per wavefront ring (registers bound it)
-  constexpr int D = kHeadDim;
+  static_assert(D == 64 || D == 128 || D == 256, "head dims built");
+  constexpr int KS = D / 32;   // k-steps of the S^T MFMA (32 dims each)
+  constexpr int DB = D / 16;   // 16-dim blocks of the P.V MFMA
+  constexpr int NV = D / 32;   // 16-byte V loads per lane and tile
+  constexpr int CH = D / 8;    // 16-byte chunks per V row
+  constexpr int kVRow = v_row<D>();
+  // tiles per wavefront ring (registers bound it)
+  constexpr int DEPTH = (RB >= 2 || D >= 256) ? 2 : 3;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -73,17 +85,17 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
 
   // Q-block (B operands) and this wave's first 64 page ids, before the
   // context length arrives.
-  bf16x8 qb[RB][4];
+  bf16x8 qb[RB][KS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = 16 * rb + n;
     if (r < R) {
       const uint16_t* qrow = p.q + unit_row(p, q0, g, G, r) * D + 8 * c;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qb[rb][j] = as_bf16x8(ld16(qrow + 32 * j));
+      for (int j = 0; j < KS; ++j) qb[rb][j] = as_bf16x8(ld16(qrow + 32 * j));
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qb[rb][j] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      for (int j = 0; j < KS; ++j) qb[rb][j] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
   }
   const int t_begin = ev.t_begin;
@@ -106,7 +118,9 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   const int lim_lo = p.causal ? L - qn + 1 : L;
 
   const uint16_t* kbase = p.k_pool + (int64_t)g * p.stride_head + (int64_t)n * p.stride_token + 8 * c;
-  const uint16_t* vbase = p.v_pool + (int64_t)g * p.stride_head + (int64_t)c * p.stride_token + 8 * n;
+  // V load u of this lane: chunk (64u + lane) of the tile's 16 x CH row chunks
+  const uint16_t* vbase = p.v_pool + (int64_t)g * p.stride_head +
+                          (int64_t)(lane / CH) * p.stride_token + 8 * (lane % CH);
   uint16_t* vt = reinterpret_cast<uint16_t*>(sm_buf) + wave * 16 * kVRow;
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   // transposing read of lane (c, n): row 4c + n/4, dims 4(n%4) (+16 per block)
@@ -116,19 +130,19 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     const int i = lane + 64 * chunk;
     pages = (i < nt) ? bt[t_begin + wave + W * i] : 0;
   };
-  auto issue = [&](int i, uint4 (&kr)[4], uint4 (&vr)[4]) {
+  auto issue = [&](int i, uint4 (&kr)[KS], uint4 (&vr)[NV]) {
     const int64_t page = readlane(pages, i & 63);
     const uint16_t* kp = kbase + page * p.stride_page;
     const uint16_t* vp = vbase + page * p.stride_page;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kr[j] = ld16(kp + 32 * j);
+    for (int j = 0; j < KS; ++j) kr[j] = ld16(kp + 32 * j);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = ld16(vp + (int64_t)(4 * r) * p.stride_token);
+    for (int u = 0; u < NV; ++u) vr[u] = ld16(vp + (int64_t)(64 / CH * u) * p.stride_token);
   };
 
-  f32x4 acc[8][RB];
+  f32x4 acc[DB][RB];
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[db][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m[RB], lsum[RB];
@@ -138,16 +152,16 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     lsum[rb] = 0.f;
   }
 
-  uint4 kr[DEPTH][4], vr[DEPTH][4];
+  uint4 kr[DEPTH][KS], vr[DEPTH][NV];
 
-  auto process = [&](uint4 (&kc)[4], uint4 (&vc)[4], int i) {
+  auto process = [&](uint4 (&kc)[KS], uint4 (&vc)[NV], int i) {
     const int t = t_begin + wave + W * i;
     f32x4 s[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       s[rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < KS; ++j)
         s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[j]), qb[rb][j], s[rb], 0, 0, 0);
     }
     const int key0 = t * kDecodeTile + 4 * c;
@@ -176,7 +190,7 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
         m[rb] = need ? tmax[rb] : m[rb];
         lsum[rb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) acc[db][rb] *= alpha;
+        for (int db = 0; db < DB; ++db) acc[db][rb] *= alpha;
       }
     }
 
@@ -204,14 +218,14 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
 
     if (t * kDecodeTile + kDecodeTile > L) {  // last tile: drop stale V rows
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (t * kDecodeTile + c + 4 * r >= L) vc[r] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < NV; ++u)
+        if (t * kDecodeTile + (64 * u + lane) / CH >= L) vc[u] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<uint4*>(vt + (c + 4 * r) * kVRow + 8 * n) = vc[r];
+    for (int u = 0; u < NV; ++u)
+      *reinterpret_cast<uint4*>(vt + ((64 * u + lane) / CH) * kVRow + 8 * (lane % CH)) = vc[u];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < DB; ++db) {
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_off + 16 * db));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -266,7 +280,7 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     __syncthreads();  // the V tiles, or the previous block, are no longer read
     float* so = sm_buf + wave * 16 * D;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < DB; ++db)
       *reinterpret_cast<f32x4*>(so + n * D + 16 * db + 4 * c) = acc[db][rb];
     __syncthreads();
     for (int idx = tid; idx < 16 * (D / 4); idx += 64 * W) {

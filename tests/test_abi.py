@@ -80,7 +80,7 @@ def test_select_tiles_decode_and_prefill(lib):
 
 @pytest.mark.parametrize("field,value,status", [
     ("num_q_heads", 30, pa.PA_ERR_INVALID_ARG),       # Hq % Hkv != 0
-    ("head_dim", 64, pa.PA_ERR_UNSUPPORTED),
+    ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
     ("page_size", 12, pa.PA_ERR_INVALID_ARG),         # not a power of two
     ("page_size", 32, pa.PA_ERR_UNSUPPORTED),
     ("kv_stride_token", 1020, pa.PA_ERR_INVALID_ARG),  # not a multiple of 8
@@ -103,6 +103,26 @@ def test_group_sizes_built(lib):
         st, t, _ = _select(lib, _problem(num_q_heads=hq, num_kv_heads=hkv))
         assert st == pa.PA_OK, (hq, hkv)
     st, _, _ = _select(lib, _problem(num_q_heads=64, num_kv_heads=1))  # G = 64
+    assert st == pa.PA_ERR_UNSUPPORTED
+
+
+def test_head_dims_built(lib):
+    """Head dims 64 and 256 are built for decode and short query runs (the
+    short-run kernel); longer runs need the query tiles, built for 128."""
+    for d in (64, 128, 256):
+        kw = dict(head_dim=d, kv_stride_page=16 * 8 * d, kv_stride_token=8 * d, kv_stride_head=d)
+        st, t, ws = _select(lib, _problem(**kw))  # decode
+        assert st == pa.PA_OK, d
+        st, t, ws = _select(lib, _problem(max_query_len=4, total_query_tokens=16, **kw))
+        assert st == pa.PA_OK, d
+        st, _, _ = _select(lib, _problem(max_query_len=64, total_query_tokens=256, **kw))
+        assert st == (pa.PA_OK if d == 128 else pa.PA_ERR_UNSUPPORTED), d
+    # 16 rows x 256 dims per row block: at most two row blocks
+    kw = dict(head_dim=256, kv_stride_page=16 * 8 * 256, kv_stride_token=8 * 256,
+              kv_stride_head=256)
+    st, _, _ = _select(lib, _problem(max_query_len=8, total_query_tokens=32, **kw))
+    assert st == pa.PA_OK
+    st, _, _ = _select(lib, _problem(max_query_len=9, total_query_tokens=36, **kw))
     assert st == pa.PA_ERR_UNSUPPORTED
 
 
@@ -201,7 +221,7 @@ def test_cache_append_rejects_before_launch(lib):
     assert call(pb, kp=mis) == pa.PA_ERR_INVALID_ARG
     # one token per sequence unless query_start_loc is given
     assert call(_problem(total_query_tokens=9)) == pa.PA_ERR_INVALID_ARG
-    assert call(_problem(head_dim=64, kv_stride_head=64)) == pa.PA_ERR_UNSUPPORTED
+    assert call(_problem(head_dim=96, kv_stride_head=96)) == pa.PA_ERR_UNSUPPORTED
     assert call(_problem(page_size=32)) == pa.PA_ERR_UNSUPPORTED
     assert call(_problem(kv_stride_token=12)) == pa.PA_ERR_INVALID_ARG
     # nothing to write: no launch
