@@ -201,7 +201,10 @@ pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const voi
   r.piece_counts = d.piece_counts;
   r.context_lens = context_lens;
   r.group = G;
-  return from_hip(pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, stream));
+  r.unit_rows = 0;
+  const int unit_rows = (problem->max_query_len > 1 ? problem->max_query_len : 1) * G;
+  return from_hip(
+      pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, unit_rows, stream));
 }
 
 }  // namespace
@@ -366,6 +369,7 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
     r.piece_counts = even ? p.piece_counts : nullptr;
     r.context_lens = context_lens;
     r.group = G;
+    r.unit_rows = 0;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -501,6 +505,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
       r.piece_counts = d.piece_counts;
       r.context_lens = context_lens;
       r.group = G;
+      r.unit_rows = 0;
       st = from_hip(pa::launch_reduce(r, stream));
     }
     return st;
@@ -546,6 +551,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     r.piece_counts = d.piece_counts;
     r.context_lens = context_lens;
     r.group = G;
+    r.unit_rows = 0;
     st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
@@ -607,6 +613,7 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
   r.piece_counts = nullptr;
   r.context_lens = nullptr;
   r.group = 1;
+  r.unit_rows = 0;
   return from_hip(pa::launch_reduce(r, stream));
 }
 

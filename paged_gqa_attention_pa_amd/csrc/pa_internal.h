@@ -84,6 +84,11 @@ struct ReduceParams {
   const int32_t* piece_counts;
   const int32_t* context_lens;
   int32_t group;
+  // Short-run partials (rows are (token, q head) pairs): > 0 launches a
+  // (units, unit_rows) grid, workgroup (u, r) merging row r of unit u =
+  // (sequence, kv head), token r / G of the sequence (query_start_loc, or
+  // token u / Hkv when it is null), head (u % Hkv) * G + r % G.
+  int32_t unit_rows;
 };
 
 // Merge of split query tiles: one workgroup per (query tile, kv head) of the
@@ -129,8 +134,10 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 // Short-run path: merge the pieces of every (sequence, kv head) unit (rows
 // are (token, q head) pairs; piece_counts and context_lens are required,
 // query_start_loc null means one token per sequence); units = num_seqs *
-// num_kv_heads.
-hipError_t launch_unit_merge(const ReduceParams& p, int units, hipStream_t stream);
+// num_kv_heads, unit_rows = the longest run's rows (max_query_len * G).
+// Many rows merge with one workgroup per unit, few with one per (unit, row).
+hipError_t launch_unit_merge(const ReduceParams& p, int units, int unit_rows,
+                             hipStream_t stream);
 // Short query runs (1 <= q_s, q_s * G <= 64; <= 32 at head dim 256): 16-row
 // blocks per unit (1, 2 or 4; 0 when not built), resident workgroups of that
 // kernel, and the even-work launch of nw workgroups.

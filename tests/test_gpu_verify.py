@@ -30,6 +30,9 @@ VERIFY_CASES = [
     ("g16_q4", [500, 17, 2000], [4, 3, 2], 16, 1, True),
     ("noncausal", [300, 45, 1000], [6, 4, 8], 32, 8, False),
     ("long_context", [40000, 300], [4, 3], 32, 8, True),
+    # 40 sequences x 8 kv heads x 16 rows: enough rows for the per-unit merge
+    ("many_units", [17 + (97 * i) % 3000 for i in range(40)], [1 + i % 4 for i in range(40)],
+     32, 8, True),
 ]
 
 
