@@ -18,12 +18,13 @@ using verify_detail::verify_smem_floats;
 
 constexpr int kVerifyWaves = 4;
 
-// Two workgroups per CU where the accumulators allow (RB <= 2 at D <= 128),
-// so that two wavefronts per SIMD keep loads in flight; otherwise one, with
-// the accumulators in AGPRs.
+// Two workgroups per CU where the accumulators allow (at most two row blocks
+// per wavefront, which four row blocks get by pairing wavefronts, at
+// D <= 128), so that two wavefronts per SIMD keep loads in flight; otherwise
+// one, with the accumulators in AGPRs.
 template <int RB, int D>
 constexpr int verify_min_blocks() {
-  return (RB <= 2 && D <= 128) ? 2 : 1;
+  return (RB <= 4 && D <= 128) ? 2 : 1;
 }
 
 template <int G, int RB, bool PRECISE, int D>

@@ -70,10 +70,18 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   constexpr int NV = D / 32;   // 16-byte V loads per lane and tile
   constexpr int CH = D / 8;    // 16-byte chunks per V row
   constexpr int kVRow = v_row<D>();
+  // Four row blocks: the wavefronts pair up; both of a pair stream the same
+  // tiles (the second read of a tile is an L2 hit) and each keeps two of the
+  // row blocks, so its registers are those of two row blocks.
+  constexpr bool kPairs = RB >= 4;
+  constexpr int RBW = kPairs ? RB / 2 : RB;  // row blocks of one wavefront
+  constexpr int WS = kPairs ? W / 2 : W;     // tile streams of the workgroup
   // tiles per wavefront ring (registers bound it)
-  constexpr int DEPTH = (RB >= 2 || D >= 256) ? 2 : 3;
+  constexpr int DEPTH = (RBW >= 2 || D >= 256) ? 2 : 3;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int strm = kPairs ? wave >> 1 : wave;  // this wavefront's tile stream
+  const int rb0 = kPairs ? (wave & 1) * RBW : 0;  // its first row block
   const int lane = tid & 63;
   const int c = lane >> 4;
   const int n = lane & 15;
@@ -85,10 +93,10 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
 
   // Q-block (B operands) and this wave's first 64 page ids, before the
   // context length arrives.
-  bf16x8 qb[RB][KS];
+  bf16x8 qb[RBW][KS];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 16 * rb + n;
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int r = 16 * (rb0 + rb) + n;
     if (r < R) {
       const uint16_t* qrow = p.q + unit_row(p, q0, g, G, r) * D + 8 * c;
 #pragma unroll
@@ -100,19 +108,20 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   }
   const int t_begin = ev.t_begin;
   const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
-  const int t_first = t_begin + wave + W * lane;
+  const int t_first = t_begin + strm + WS * lane;
   int pages = (t_first < p.max_blocks) ? bt[t_first] : 0;
 
   const int L = p.context_lens[b];
   const int t_end = ev.t_end;
-  const int nt = (t_end - t_begin - wave + W - 1) / W > 0 ? (t_end - t_begin - wave + W - 1) / W : 0;
+  const int nt =
+      (t_end - t_begin - strm + WS - 1) / WS > 0 ? (t_end - t_begin - strm + WS - 1) / WS : 0;
 
   // keys < lim[rb] are allowed in column 16*rb + n; every column is limited
   // from key lim_lo on
-  int lim[RB];
+  int lim[RBW];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 16 * rb + n;
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int r = 16 * (rb0 + rb) + n;
     lim[rb] = (p.causal && r < R) ? L - qn + r / G + 1 : L;
   }
   const int lim_lo = p.causal ? L - qn + 1 : L;
@@ -128,7 +137,7 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
 
   auto fetch_pages = [&](int chunk) {
     const int i = lane + 64 * chunk;
-    pages = (i < nt) ? bt[t_begin + wave + W * i] : 0;
+    pages = (i < nt) ? bt[t_begin + strm + WS * i] : 0;
   };
   auto issue = [&](int i, uint4 (&kr)[KS], uint4 (&vr)[NV]) {
     const int64_t page = readlane(pages, i & 63);
@@ -140,14 +149,14 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     for (int u = 0; u < NV; ++u) vr[u] = ld16(vp + (int64_t)(64 / CH * u) * p.stride_token);
   };
 
-  f32x4 acc[DB][RB];
+  f32x4 acc[DB][RBW];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[db][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m[RB], lsum[RB];
+    for (int rb = 0; rb < RBW; ++rb) acc[db][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m[RBW], lsum[RBW];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     m[rb] = kNegInf;
     lsum[rb] = 0.f;
   }
@@ -155,10 +164,10 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   uint4 kr[DEPTH][KS], vr[DEPTH][NV];
 
   auto process = [&](uint4 (&kc)[KS], uint4 (&vc)[NV], int i) {
-    const int t = t_begin + wave + W * i;
-    f32x4 s[RB];
+    const int t = t_begin + strm + WS * i;
+    f32x4 s[RBW];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RBW; ++rb) {
       s[rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KS; ++j)
@@ -166,11 +175,11 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     }
     const int key0 = t * kDecodeTile + 4 * c;
     const bool edge = t * kDecodeTile + kDecodeTile > lim_lo;
-    float x[RB][4];
+    float x[RBW][4];
     bool need_any = false;
-    float tmax[RB];
+    float tmax[RBW];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[rb][e] = s[rb][e] * p.scale_log2;
@@ -184,7 +193,7 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     }
     if (wave_any(need_any)) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+      for (int rb = 0; rb < RBW; ++rb) {
         const bool need = tmax[rb] > m[rb] + kLazyThreshold;
         const float alpha = need ? fast_exp2(m[rb] - tmax[rb]) : 1.f;  // 0 on a first raise
         m[rb] = need ? tmax[rb] : m[rb];
@@ -196,9 +205,9 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
 
     // P (B operands of the P.V MFMA); a column with no allowed key yet keeps
     // m = -inf and gets P = 0
-    i16x4 ph[RB], pl[RB];
+    i16x4 ph[RBW], pl[RBW];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RBW; ++rb) {
       const float mm = m[rb] == kNegInf ? 0.f : m[rb];
       float pr[4];
 #pragma unroll
@@ -228,7 +237,7 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     for (int db = 0; db < DB; ++db) {
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + tr_off + 16 * db));
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+      for (int rb = 0; rb < RBW; ++rb) {
         acc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[rb], acc[db][rb], 0, 0, 0);
         if constexpr (PRECISE)
           acc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[rb], acc[db][rb], 0, 0, 0);
@@ -258,19 +267,21 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   }
 
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     lsum[rb] += shfl_xor(lsum[rb], 16);
     lsum[rb] += shfl_xor(lsum[rb], 32);
   }
 
-  // Merge the W wavefronts, one 16-column block at a time.
+  // Merge the W wavefronts, one 16-column block at a time (a wavefront that
+  // does not hold a block reports m = -inf for it and is skipped).
   __shared__ float sm_m[W][16 * RB];
   __shared__ float sm_l[W][16 * RB];
   if (c == 0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      sm_m[wave][16 * rb + n] = m[rb];
-      sm_l[wave][16 * rb + n] = lsum[rb];
+      const bool mine = rb >= rb0 && rb < rb0 + RBW;
+      sm_m[wave][16 * rb + n] = mine ? m[rb % RBW] : kNegInf;
+      sm_l[wave][16 * rb + n] = mine ? lsum[rb % RBW] : 0.f;
     }
   }
   const int S = ev.slots;
@@ -279,9 +290,11 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     if (16 * rb >= R) break;
     __syncthreads();  // the V tiles, or the previous block, are no longer read
     float* so = sm_buf + wave * 16 * D;
+    if (rb >= rb0 && rb < rb0 + RBW) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<f32x4*>(so + n * D + 16 * db + 4 * c) = acc[db][rb];
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(so + n * D + 16 * db + 4 * c) = acc[db][rb % RBW];
+    }
     __syncthreads();
     for (int idx = tid; idx < 16 * (D / 4); idx += 64 * W) {
       const int col = idx / (D / 4);
