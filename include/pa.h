@@ -70,9 +70,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment          */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128/256,
                              page size != 16, G not in {1,2,4,8,16,32}, and
-                             at head_dim 64/256 query runs beyond the
-                             short-run kernel (max_query_len * G > 64, > 32
-                             at 256)                                        */
+                             at head_dim 256 query runs beyond the short-run
+                             kernel (max_query_len * G > 32)                */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
   PA_ERR_HIP = 4          /* a HIP launch failed                            */
 } pa_status;

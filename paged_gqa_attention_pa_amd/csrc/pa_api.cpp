@@ -86,12 +86,13 @@ bool verify_path(const pa_problem* pb) {
   return pb->max_query_len >= 2 && pa::verify_row_blocks(G, pb->max_query_len, pb->head_dim) > 0;
 }
 
-// Head dims other than 128 are built for decode and short query runs only
-// (the query-tile kernel is laid out for 128).
+// Head dim 256 is built for decode and short query runs only (the query-tile
+// kernel is built for 64 and 128: its LDS ring of four K and five V tiles
+// would not fit at 256).
 pa_status check_attention(const pa_problem* pb) {
   pa_status st = check_problem(pb);
   if (st != PA_OK) return st;
-  if (pb->head_dim != kHeadDim && !verify_path(pb)) return PA_ERR_UNSUPPORTED;
+  if (pb->head_dim == 256 && !verify_path(pb)) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -392,7 +393,8 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   // unified launch G = 16 has no decode workgroups: its single-token
   // sequences take the prefill tiles.
   const bool decode_only = problem->max_query_len <= 1;
-  const bool decode_rows = decode_only || (may_hold_decode_rows(problem) && G <= 8);
+  const bool decode_rows =
+      decode_only || (may_hold_decode_rows(problem) && G <= 8 && problem->head_dim == kHeadDim);
   const int S = decode_rows ? tiles->num_splits : 1;
   const bool even = decode_rows && even_grid(tiles);
   const int TS = tile_splits_of(problem, tiles);
@@ -514,11 +516,12 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   const int64_t nx = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
   int64_t n_dec = decode_rows ? (int64_t)problem->num_seqs * problem->num_kv_heads * S : 0;
   if (even) {
-    n_dec = pa::unified_resident(G, precise);
+    n_dec = pa::unified_resident(G, precise, problem->head_dim);
     if (n_dec <= 0) return PA_ERR_HIP;
   }
   if (nx * problem->num_kv_heads * TS + n_dec > 0x7fffffff) return PA_ERR_UNSUPPORTED;
-  if ((st = from_hip(pa::launch_prefill(p, d, G, (int)nx, (int)n_dec, precise, stream))) != PA_OK)
+  if ((st = from_hip(pa::launch_prefill(p, d, G, (int)nx, (int)n_dec, precise, problem->head_dim,
+                                        stream))) != PA_OK)
     return st;
   if (TS > 1) {
     pa::TileMergeParams m;
@@ -534,7 +537,8 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     m.decode_rows_apart = p.decode_rows_apart;
     m.tile_splits = TS;
     m.out_f32 = out_f32;
-    if ((st = from_hip(pa::launch_tile_merge(m, (int)nx, stream))) != PA_OK) return st;
+    if ((st = from_hip(pa::launch_tile_merge(m, (int)nx, problem->head_dim, stream))) != PA_OK)
+      return st;
   }
   if (decode_rows && S > 1) {
     pa::ReduceParams r;

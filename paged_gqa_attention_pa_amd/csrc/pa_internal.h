@@ -127,9 +127,9 @@ int decode_even_resident(int group, int waves);
 // Prefill tiles (nx x Hkv workgroups) and n_dec decode workgroups (split x
 // Hkv x B, for the single-token sequences of a mixed batch) in one launch.
 hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
-                          int n_dec, bool precise_p, hipStream_t stream);
+                          int n_dec, bool precise_p, int head_dim, hipStream_t stream);
 // Workgroups of the unified prefill kernel that fit on the device at once.
-int unified_resident(int group, bool precise_p);
+int unified_resident(int group, bool precise_p, int head_dim);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 // Short-run path: merge the pieces of every (sequence, kv head) unit (rows
 // are (token, q head) pairs; piece_counts and context_lens are required,
@@ -146,6 +146,6 @@ int verify_resident(int group, int rb, bool precise_p, int head_dim);
 hipError_t launch_verify(const DecodeParams& p, int group, int rb, bool precise_p, int head_dim,
                          int nw, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
-hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream);
+hipError_t launch_tile_merge(const TileMergeParams& p, int nx, int head_dim, hipStream_t stream);
 
 }  // namespace pa

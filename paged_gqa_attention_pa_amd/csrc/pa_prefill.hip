@@ -18,39 +18,40 @@ namespace {
 using decode_detail::decode_body;
 using decode_detail::decode_even_body;
 using decode_detail::decode_smem_floats;
-using prefill_detail::kPrefillSmemBytes;
+using prefill_detail::prefill_smem_bytes;
 using prefill_detail::kThreads;
 using prefill_detail::prefill_body;
 
 constexpr int kDecodeWaves = kThreads / 64;
 
-// Decode workgroups run with all kThreads threads; G = 16 is not built that
-// way, so for it every sequence takes the prefill tiles.
-template <int G>
+// Decode workgroups run with all kThreads threads; G = 16 and 32 are not
+// built that way, nor head dims other than 128, so for those every sequence
+// takes the prefill tiles.
+template <int G, int D>
 constexpr bool decode_part_built() {
-  return G * kDecodeWaves <= 64;
+  return D == kHeadDim && G * kDecodeWaves <= 64;
 }
 
-template <int G>
+template <int G, int D>
 constexpr int unified_smem_bytes() {
-  if constexpr (decode_part_built<G>()) {
-    return kPrefillSmemBytes > decode_smem_floats<G, kDecodeWaves>() * 4
-               ? kPrefillSmemBytes
+  if constexpr (decode_part_built<G, D>()) {
+    return prefill_smem_bytes<D>() > decode_smem_floats<G, kDecodeWaves>() * 4
+               ? prefill_smem_bytes<D>()
                : decode_smem_floats<G, kDecodeWaves>() * 4;
   } else {
-    return kPrefillSmemBytes;
+    return prefill_smem_bytes<D>();
   }
 }
 
-template <int G, bool PRECISE>
+template <int G, bool PRECISE, int D>
 __global__ __launch_bounds__(kThreads, 2) void unified_kernel(PrefillParams pp, DecodeParams dp,
                                                               int nx) {
-  __shared__ __attribute__((aligned(16))) char smem[unified_smem_bytes<G>()];
+  __shared__ __attribute__((aligned(16))) char smem[unified_smem_bytes<G, D>()];
   const int n_pre = nx * pp.num_kv_heads * pp.tile_splits;
   const int id = blockIdx.x;
   if (id < n_pre) {
-    prefill_body<G, PRECISE>(pp, id, nx, smem);
-  } else if constexpr (decode_part_built<G>()) {
+    prefill_body<G, PRECISE, D>(pp, id, nx, smem);
+  } else if constexpr (decode_part_built<G, D>()) {
     const int d = id - n_pre;
     if (dp.piece_counts) {  // even-work grid over the single-token sequences
       decode_even_body<G, kDecodeWaves>(dp, d, gridDim.x - n_pre, reinterpret_cast<float*>(smem));
@@ -63,68 +64,63 @@ __global__ __launch_bounds__(kThreads, 2) void unified_kernel(PrefillParams pp, 
   }
 }
 
-template <bool PRECISE>
-hipError_t launch_t(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
-                    int n_dec, hipStream_t stream) {
-  const dim3 grid((unsigned)(nx * pp.num_kv_heads * pp.tile_splits + n_dec));
-  const dim3 block(kThreads);
-  switch (group) {
-    case 1: hipLaunchKernelGGL((unified_kernel<1, PRECISE>), grid, block, 0, stream, pp, dp, nx); break;
-    case 2: hipLaunchKernelGGL((unified_kernel<2, PRECISE>), grid, block, 0, stream, pp, dp, nx); break;
-    case 4: hipLaunchKernelGGL((unified_kernel<4, PRECISE>), grid, block, 0, stream, pp, dp, nx); break;
-    case 8: hipLaunchKernelGGL((unified_kernel<8, PRECISE>), grid, block, 0, stream, pp, dp, nx); break;
-    case 16:
-      if (n_dec != 0) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((unified_kernel<16, PRECISE>), grid, block, 0, stream, pp, dp, nx);
-      break;
-    case 32:
-      if (n_dec != 0) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((unified_kernel<32, PRECISE>), grid, block, 0, stream, pp, dp, nx);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <bool PRECISE>
+template <bool PRECISE, int D>
 const void* unified_ptr(int group) {
   switch (group) {
-    case 1: return reinterpret_cast<const void*>(&unified_kernel<1, PRECISE>);
-    case 2: return reinterpret_cast<const void*>(&unified_kernel<2, PRECISE>);
-    case 4: return reinterpret_cast<const void*>(&unified_kernel<4, PRECISE>);
-    case 8: return reinterpret_cast<const void*>(&unified_kernel<8, PRECISE>);
-    case 16: return reinterpret_cast<const void*>(&unified_kernel<16, PRECISE>);
-    case 32: return reinterpret_cast<const void*>(&unified_kernel<32, PRECISE>);
+    case 1: return reinterpret_cast<const void*>(&unified_kernel<1, PRECISE, D>);
+    case 2: return reinterpret_cast<const void*>(&unified_kernel<2, PRECISE, D>);
+    case 4: return reinterpret_cast<const void*>(&unified_kernel<4, PRECISE, D>);
+    case 8: return reinterpret_cast<const void*>(&unified_kernel<8, PRECISE, D>);
+    case 16: return reinterpret_cast<const void*>(&unified_kernel<16, PRECISE, D>);
+    case 32: return reinterpret_cast<const void*>(&unified_kernel<32, PRECISE, D>);
     default: return nullptr;
   }
 }
 
+const void* unified_kernel_of(int group, bool precise, int head_dim) {
+  if (head_dim == 64) return precise ? unified_ptr<true, 64>(group) : unified_ptr<false, 64>(group);
+  if (head_dim == kHeadDim)
+    return precise ? unified_ptr<true, kHeadDim>(group) : unified_ptr<false, kHeadDim>(group);
+  return nullptr;
+}
+
 }  // namespace
 
-int unified_resident(int group, bool precise_p) {
+int unified_resident(int group, bool precise_p, int head_dim) {
   constexpr int kDevs = 64;
-  static std::atomic<int> cache[kDevs][6][2];
+  static std::atomic<int> cache[kDevs][6][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : group == 16 ? 4 : 5;
-  const int cached = cache[dev][gi][precise_p].load(std::memory_order_relaxed);
+  std::atomic<int>& slot = cache[dev][gi][precise_p ? 1 : 0][head_dim == 64 ? 0 : 1];
+  const int cached = slot.load(std::memory_order_relaxed);
   if (cached > 0) return cached;
-  const void* k = precise_p ? unified_ptr<true>(group) : unified_ptr<false>(group);
+  const void* k = unified_kernel_of(group, precise_p, head_dim);
   int cus = 0, per_cu = 0;
   if (!k || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess)
     return 0;
   const int n = cus * (per_cu > 0 ? per_cu : 1);
-  cache[dev][gi][precise_p].store(n, std::memory_order_relaxed);
+  slot.store(n, std::memory_order_relaxed);
   return n;
 }
 
 hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
-                          int n_dec, bool precise_p, hipStream_t stream) {
+                          int n_dec, bool precise_p, int head_dim, hipStream_t stream) {
   if ((int64_t)nx * pp.num_kv_heads + n_dec <= 0) return hipSuccess;
-  if ((int64_t)nx * pp.num_kv_heads + n_dec > 0x7fffffff) return hipErrorInvalidValue;
-  return precise_p ? launch_t<true>(pp, dp, group, nx, n_dec, stream)
-                   : launch_t<false>(pp, dp, group, nx, n_dec, stream);
+  if ((int64_t)nx * pp.num_kv_heads * pp.tile_splits + n_dec > 0x7fffffff)
+    return hipErrorInvalidValue;
+  const void* k = unified_kernel_of(group, precise_p, head_dim);
+  if (!k) return hipErrorInvalidValue;
+  // decode workgroups exist only where the kernel holds the decode part
+  if (n_dec != 0 && !(head_dim == kHeadDim && group * kDecodeWaves <= 64))
+    return hipErrorInvalidValue;
+  PrefillParams a = pp;
+  DecodeParams b = dp;
+  int c = nx;
+  void* args[] = {&a, &b, &c};
+  const unsigned grid = (unsigned)((int64_t)nx * pp.num_kv_heads * pp.tile_splits + n_dec);
+  return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace pa

@@ -42,10 +42,17 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;   // Q-block rows per workgroup
 constexpr int kKvTile = 32;          // keys per inner step
-constexpr int kLdsStride = kHeadDim + 8;   // K: bf16 elements per LDS row (272 B)
-constexpr int kVStride = kHeadDim + 48;    // V: bf16 elements per LDS row (352 B): the
-                                           // four rows of a transposing read group
-                                           // fall on disjoint banks
+// K and V LDS rows (bf16 elements) for head dim D: K rows padded by 8
+// (272 B at D = 128), V rows by 48 (352 B at 128: the four rows of a
+// transposing read group fall on disjoint banks).
+template <int D>
+constexpr int k_stride() {
+  return D + 8;
+}
+template <int D>
+constexpr int v_stride() {
+  return D + 48;
+}
 constexpr int kKBufs = 4;                 // LDS K tile buffers
 constexpr int kVBufs = 5;                 // LDS V tile buffers (V is read one step later)
 constexpr int kPageCache = 2048;          // block-table entries staged in LDS (32k keys)
@@ -99,16 +106,23 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool 
 }
 
 // LDS bytes prefill_body needs from its caller (K tiles, V^T tiles, page ids).
-constexpr int kPrefillSmemBytes =
-    kKBufs * kKvTile * kLdsStride * 2 + kVBufs * kKvTile * kVStride * 2 + kPageCache * 4;
+template <int D = kHeadDim>
+constexpr int prefill_smem_bytes() {
+  return kKBufs * kKvTile * k_stride<D>() * 2 + kVBufs * kKvTile * v_stride<D>() * 2 +
+         kPageCache * 4;
+}
 
 // One workgroup of kThreads threads: query tile / split / KV head number `id`
-// of the 1-D prefill grid (nx tiles x tile_splits x Hkv).  smem:
-// kPrefillSmemBytes, 16-byte aligned.
-template <int G, bool PRECISE>
+// of the 1-D prefill grid (nx tiles x tile_splits x Hkv), head dim D (64 or
+// 128).  smem: prefill_smem_bytes<D>(), 16-byte aligned.
+template <int G, bool PRECISE, int D = kHeadDim>
 __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int nx,
                                              char* smem) {
-  constexpr int D = kHeadDim;
+  static_assert(D == 64 || D == 128, "query tiles are built for head dims 64 and 128");
+  constexpr int kLdsStride = k_stride<D>();
+  constexpr int kVStride = v_stride<D>();
+  constexpr int KS = D / 16;  // k-steps of the S^T MFMA
+  constexpr int MT = D / 32;  // 32-dim M tiles of O^T
   constexpr int QT = kRows / G;
   // 1-D grid: id -> (kv head, split, query tile).  Consecutive ids go to
   // different XCDs, so with Hkv = 8 each XCD serves one KV head and its K/V
@@ -152,12 +166,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     return;
   }
 
-  // Q^T operand: lane holds Q[row][16ks + 8*half .. +8] for ks = 0..7.
-  bf16x8 qb[8];
+  // Q^T operand: lane holds Q[row][16ks + 8*half .. +8] for ks < KS.
+  bf16x8 qb[KS];
   {
     const uint16_t* qrow = p.q + ((int64_t)(q0 + qi) * p.num_q_heads + g * G + h) * D + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
       qb[ks] = row_valid ? as_bf16x8(ld16(qrow + 16 * ks)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
@@ -168,14 +182,20 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   auto v_lds =
       reinterpret_cast<uint16_t(*)[kKvTile * kVStride]>(smem + kKBufs * kKvTile * kLdsStride * 2);
 
-  // Tile loader: thread t stages 16 bytes of K and 16 bytes of V of key
-  // t / 16, dims 8*(t%16) .. +7 (a wavefront moves four whole 256-byte rows
-  // of each), so every wavefront does the same staging work.  Loads are
-  // unconditional (a key past the context reads a valid page and its V row
-  // is zeroed when stored), so no load sits under a branch and the compiler
-  // keeps them in flight across the loop.
+  // Tile loader.  D = 128: thread t stages 16 bytes of K and 16 bytes of V
+  // of key t / 16, dims 8*(t%16) .. +7 (a wavefront moves four whole
+  // 256-byte rows of each), so every wavefront does the same staging work.
+  // D = 64: a tile is 256 chunks of 16 bytes for K and as many for V, so
+  // wavefronts 0..3 stage K and 4..7 stage V.  Loads are unconditional (a
+  // key past the context reads a valid page and its V row is zeroed when
+  // stored), so no load sits under a branch and the compiler keeps them in
+  // flight across the loop.
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  constexpr bool kSplitKV = 2 * kKvTile * CH <= kThreads;
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
-  const int lkey = tid >> 4, ldc = tid & 15;
+  const int ti = kSplitKV ? tid % (kKvTile * CH) : tid;
+  const bool stage_v = kSplitKV && tid >= kKvTile * CH;  // wavefront-uniform
+  const int lkey = ti / CH, ldc = ti % CH;
   const int64_t loff = (int64_t)g * p.stride_head + (int64_t)(lkey % kPage) * p.stride_token + 8 * ldc;
   const char* kth = reinterpret_cast<const char*>(p.k_pool + loff);
   const char* vth = reinterpret_cast<const char*>(p.v_pool + loff);
@@ -188,20 +208,34 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   constexpr int kWinTiles = kPageCache * kPage / kKvTile;
   const int nblk = (L + kPage - 1) / kPage;  // valid block-table entries
   int win0 = 0;                              // first key tile of the window
-  // tile t of the window -> r[0] = K, r[1] = V
+  // tile t of the window -> r[0] = K, r[1] = V (split: r[0] = this thread's
+  // K or V chunk)
   auto load_tile = [&](int t, uint4 (&r)[2]) {
     const uint64_t off =
         (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + lkey / kPage] * page_bytes;
-    r[0] = *reinterpret_cast<const uint4*>(kth + off);
-    r[1] = *reinterpret_cast<const uint4*>(vth + off);
+    if constexpr (kSplitKV) {
+      r[0] = *reinterpret_cast<const uint4*>((stage_v ? vth : kth) + off);
+    } else {
+      r[0] = *reinterpret_cast<const uint4*>(kth + off);
+      r[1] = *reinterpret_cast<const uint4*>(vth + off);
+    }
   };
   auto store_tile = [&](int t, int kbuf, int vbuf, const uint4 (&r)[2]) {
-    *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) = r[0];
     // V rows past the context are zeroed: stale data (even NaN) must not
     // reach O through a zero weight
     const bool tail = (win0 + t + 1) * kKvTile > L;  // uniform
-    const uint4 v = (tail && (win0 + t) * kKvTile + lkey >= L) ? make_uint4(0, 0, 0, 0) : r[1];
-    *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) = v;
+    const bool dead = tail && (win0 + t) * kKvTile + lkey >= L;
+    if constexpr (kSplitKV) {
+      if (stage_v)
+        *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
+            dead ? make_uint4(0, 0, 0, 0) : r[0];
+      else
+        *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) = r[0];
+    } else {
+      *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) = r[0];
+      *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
+          dead ? make_uint4(0, 0, 0, 0) : r[1];
+    }
   };
   // Transposing V reads: lane (group gq = lane / 16, r = lane % 16) points
   // at key 4*half + r/4 (+16kk, +8 for the second read), dims
@@ -210,14 +244,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // 16kk + 8*(j/4) + 4*half + j%4.
   const int vr_off = (4 * half + (lane & 15) / 4) * kVStride + 16 * ((lane >> 4) & 1) +
                      4 * (lane & 3);
-  // S^T = K Q^T for the tile in buffer buf, D = 128 in 8 steps of 16.  All
-  // eight K operands are read before the first MFMA (the scheduling barrier
+  // S^T = K Q^T for the tile in buffer buf, D in KS steps of 16.  All K
+  // operands are read before the first MFMA (the scheduling barrier
   // keeps the compiler from sinking each read next to its MFMA, which would
   // put an LDS round trip between every pair of dependent MFMAs).
   auto qk = [&](int buf, f32x16& st) {
-    bf16x8 ka[8];
+    bf16x8 ka[KS];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       // two 8-byte LDS reads: measured faster than one 16-byte read on gfx950
       const uint16_t* kr = &k_lds[buf][n * kLdsStride + 16 * ks + 8 * half];
       const uint2 a0 = *reinterpret_cast<const uint2*>(kr);
@@ -228,13 +262,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
 #pragma unroll
     for (int e = 0; e < 16; ++e) st[e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], st, 0, 0, 0);
   };
 
-  f32x16 o[4];
+  f32x16 o[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[mt][e] = 0.f;
   float m = kNegInf, lsum = 0.f;
@@ -269,7 +303,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       m = m_new;
       lsum *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[mt][e] *= alpha;
     }
@@ -309,9 +343,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       if constexpr (PRECISE)
         pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2],
                                                     pl[4 * kk + 3]));
-      bf16x8 va[4];
+      bf16x8 va[MT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         // element offsets / 4: one i16x4 is 4 bf16
         lds_i16x4* at = vb + (16 * kk * kVStride + 32 * mt) / 4;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at);
@@ -322,7 +356,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pb, o[mt], 0, 0, 0);
         if constexpr (PRECISE)
           o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt], pbl, o[mt], 0, 0, 0);
@@ -391,7 +425,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   if (nsplit > 1) {  // partial of this run: normalised O and its lse
     float* dst = p.tpart_o + (orow * nsplit + split) * D;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int d = 32 * mt + 8 * rb + 4 * half;
@@ -403,7 +437,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     return;
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int d = 32 * mt + 8 * rb + 4 * half;

@@ -309,11 +309,11 @@ __global__ __launch_bounds__(kThreads) void unit_merge_kernel(ReduceParams p) {
 // rows per step and keeps four steps (eight rows) of loads in flight.
 constexpr int kMergeRowsPerIter = 8;
 
-template <int S>
+template <int S, int D>
 __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(TileMergeParams p,
                                                                              int nx) {
   using prefill_detail::find_tile;
-  constexpr int D = kHeadDim;
+  constexpr int DPL = D / 32;  // dims per lane: 32 lanes cover a row
   const int g = blockIdx.x % p.num_kv_heads;
   const int x = nx - 1 - blockIdx.x / p.num_kv_heads;
   int s, qtile;
@@ -343,18 +343,27 @@ __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(Ti
       M[u] = kNegInf;
     }
     float lse_v[kMergeRowsPerIter / 2][S];
-    float4 v[kMergeRowsPerIter / 2][S];
+    float v[kMergeRowsPerIter / 2][S][DPL];
 #pragma unroll
     for (int u = 0; u < kMergeRowsPerIter / 2; ++u)
 #pragma unroll
       for (int k = 0; k < S; ++k) {
         lse_v[u][k] = p.tpart_lse[orow[u] * S + k];
-        v[u][k] = *reinterpret_cast<const float4*>(p.tpart_o + (orow[u] * S + k) * D + 4 * dl);
+        const float* src = p.tpart_o + (orow[u] * S + k) * D + DPL * dl;
+        if constexpr (DPL == 4) {
+          const float4 t = *reinterpret_cast<const float4*>(src);
+          v[u][k][0] = t.x; v[u][k][1] = t.y; v[u][k][2] = t.z; v[u][k][3] = t.w;
+        } else {
+          const float2 t = *reinterpret_cast<const float2*>(src);
+          v[u][k][0] = t.x; v[u][k][1] = t.y;
+        }
         M[u] = fmaxf(M[u], lse_v[u][k]);
       }
 #pragma unroll
     for (int u = 0; u < kMergeRowsPerIter / 2; ++u) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float acc[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
       float wsum = 0.f;
       if (M[u] != kNegInf) {
 #pragma unroll
@@ -363,21 +372,29 @@ __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(Ti
           const bool on = lse_v[u][k] != kNegInf;
           const float w = on ? fast_exp2((lse_v[u][k] - M[u]) * kLog2e) : 0.f;
           wsum += w;
-          acc.x = fmaf(w, on ? v[u][k].x : 0.f, acc.x);
-          acc.y = fmaf(w, on ? v[u][k].y : 0.f, acc.y);
-          acc.z = fmaf(w, on ? v[u][k].z : 0.f, acc.z);
-          acc.w = fmaf(w, on ? v[u][k].w : 0.f, acc.w);
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, on ? v[u][k][e] : 0.f, acc[e]);
         }
       }
       const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-      acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] *= inv;
       if (!valid[u]) continue;
-      const int64_t off = orow[u] * D + 4 * dl;
-      if (p.out_f32) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) = acc;
+      const int64_t off = orow[u] * D + DPL * dl;
+      if constexpr (DPL == 4) {
+        if (p.out_f32)
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) =
+              make_float4(acc[0], acc[1], acc[2], acc[3]);
+        else
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + off) =
+              make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
       } else {
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + off) =
-            make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+        if (p.out_f32)
+          *reinterpret_cast<float2*>(reinterpret_cast<float*>(p.out) + off) =
+              make_float2(acc[0], acc[1]);
+        else
+          *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.out) + off) =
+              pack_bf16x2(acc[0], acc[1]);
       }
       if (p.lse && dl == 0)
         p.lse[orow[u]] = (M[u] == kNegInf) ? kNegInf : M[u] + fast_log2(wsum) * kLn2;
@@ -387,20 +404,27 @@ __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(Ti
 
 }  // namespace
 
-hipError_t launch_tile_merge(const TileMergeParams& p, int nx, hipStream_t stream) {
-  if (nx <= 0) return hipSuccess;
+template <int D>
+hipError_t launch_tile_merge_d(const TileMergeParams& p, int nx, hipStream_t stream) {
   const dim3 grid((unsigned)(nx * p.num_kv_heads)), block(prefill_detail::kThreads);
   switch (p.tile_splits) {
-    case 2: hipLaunchKernelGGL(tile_merge_kernel<2>, grid, block, 0, stream, p, nx); break;
-    case 3: hipLaunchKernelGGL(tile_merge_kernel<3>, grid, block, 0, stream, p, nx); break;
-    case 4: hipLaunchKernelGGL(tile_merge_kernel<4>, grid, block, 0, stream, p, nx); break;
-    case 5: hipLaunchKernelGGL(tile_merge_kernel<5>, grid, block, 0, stream, p, nx); break;
-    case 6: hipLaunchKernelGGL(tile_merge_kernel<6>, grid, block, 0, stream, p, nx); break;
-    case 7: hipLaunchKernelGGL(tile_merge_kernel<7>, grid, block, 0, stream, p, nx); break;
-    case 8: hipLaunchKernelGGL(tile_merge_kernel<8>, grid, block, 0, stream, p, nx); break;
+    case 2: hipLaunchKernelGGL((tile_merge_kernel<2, D>), grid, block, 0, stream, p, nx); break;
+    case 3: hipLaunchKernelGGL((tile_merge_kernel<3, D>), grid, block, 0, stream, p, nx); break;
+    case 4: hipLaunchKernelGGL((tile_merge_kernel<4, D>), grid, block, 0, stream, p, nx); break;
+    case 5: hipLaunchKernelGGL((tile_merge_kernel<5, D>), grid, block, 0, stream, p, nx); break;
+    case 6: hipLaunchKernelGGL((tile_merge_kernel<6, D>), grid, block, 0, stream, p, nx); break;
+    case 7: hipLaunchKernelGGL((tile_merge_kernel<7, D>), grid, block, 0, stream, p, nx); break;
+    case 8: hipLaunchKernelGGL((tile_merge_kernel<8, D>), grid, block, 0, stream, p, nx); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_tile_merge(const TileMergeParams& p, int nx, int head_dim, hipStream_t stream) {
+  if (nx <= 0) return hipSuccess;
+  if (head_dim == 64) return launch_tile_merge_d<64>(p, nx, stream);
+  if (head_dim == kHeadDim) return launch_tile_merge_d<kHeadDim>(p, nx, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_unit_merge(const ReduceParams& p, int units, int unit_rows,

@@ -108,7 +108,8 @@ def test_group_sizes_built(lib):
 
 def test_head_dims_built(lib):
     """Head dims 64 and 256 are built for decode and short query runs (the
-    short-run kernel); longer runs need the query tiles, built for 128."""
+    short-run kernel); longer runs need the query tiles, built for 64 and
+    128."""
     for d in (64, 128, 256):
         kw = dict(head_dim=d, kv_stride_page=16 * 8 * d, kv_stride_token=8 * d, kv_stride_head=d)
         st, t, ws = _select(lib, _problem(**kw))  # decode
@@ -116,7 +117,7 @@ def test_head_dims_built(lib):
         st, t, ws = _select(lib, _problem(max_query_len=4, total_query_tokens=16, **kw))
         assert st == pa.PA_OK, d
         st, _, _ = _select(lib, _problem(max_query_len=64, total_query_tokens=256, **kw))
-        assert st == (pa.PA_OK if d == 128 else pa.PA_ERR_UNSUPPORTED), d
+        assert st == (pa.PA_ERR_UNSUPPORTED if d == 256 else pa.PA_OK), d
     # 16 rows x 256 dims per row block: at most two row blocks
     kw = dict(head_dim=256, kv_stride_page=16 * 8 * 256, kv_stride_token=8 * 256,
               kv_stride_head=256)

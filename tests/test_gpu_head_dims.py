@@ -3,8 +3,8 @@
 Decode and short query runs at these head dims run on the short-run kernel
 (one Q-block per (sequence, kv head) unit, MFMA for both products); the
 paged append copies rows of any head dim bit for bit.  Longer query runs
-need the query-tile kernel, built for head dim 128 only: pa_prefill reports
-them as unsupported.
+take the query-tile kernel, built for head dims 64 and 128: at 256
+pa_prefill reports them as unsupported.
 """
 import numpy as np
 import pytest
@@ -78,10 +78,50 @@ def test_append_head_dim(dev, d):
     append_and_check(b, kn, vn, f"append D={d}")
 
 
-@pytest.mark.parametrize("d", [64, 256])
-def test_long_runs_unsupported(dev, d):
-    spec = workloads.small_spec(f"long_d{d}", seed=970, contexts=[300], queries=[100],
-                                head_dim=d, decode_layout=False)
+PREFILL_D64 = [
+    # (name, contexts, query lens, causal)
+    ("chunks", [300, 77, 1000, 33], [140, 77, 31, 33], True),
+    ("tiles", [32, 64, 65, 200], [32, 64, 65, 129], True),
+    ("noncausal", [300, 50], [100, 7], False),
+    ("decode_rows", [900, 40, 260, 513], [1, 1, 100, 200], True),
+    ("long_context", [40000, 300], [32, 20], True),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql,causal", PREFILL_D64, ids=[c[0] for c in PREFILL_D64])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_prefill_head_dim_64(dev, name, ctx, ql, causal, out_dtype):
+    """Query tiles at head dim 64 (K and V staged by separate wavefront halves)."""
+    log(f"[prefill D=64 {name} {out_dtype}]")
+    spec = workloads.small_spec(f"pf64_{name}", seed=980 + sum(ql), contexts=ctx, queries=ql,
+                                head_dim=64, causal=causal, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    T = sum(ql) * spec.num_q_heads
+    rows = None
+    if T > 8192:
+        rng = np.random.default_rng(3)
+        rows = np.unique(np.concatenate([rng.choice(T, 4096, replace=False), [0, T - 1]]))
+    out, lse = run_prefill(b, out_dtype)
+    compare(b, out, lse, rows=rows, label=f"prefill D=64 {name}")
+
+
+@pytest.mark.parametrize("ts", [2, 5])
+def test_prefill_head_dim_64_tile_splits(dev, ts):
+    log(f"[prefill D=64 tile splits {ts}]")
+    spec = workloads.small_spec("pf64_ts", seed=990 + ts, contexts=[2100, 1500], queries=[300, 200],
+                                head_dim=64, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    rng = np.random.default_rng(ts)
+    T = 500 * spec.num_q_heads
+    rows = np.unique(np.concatenate([rng.choice(T, 4096, replace=False), [0, T - 1]]))
+    for dt in (torch.bfloat16, torch.float32):
+        out, lse = run_prefill(b, dt, tile_splits=ts, stale_workspace=True)
+        compare(b, out, lse, rows=rows, label=f"prefill D=64 ts={ts} {dt}")
+
+
+def test_long_runs_unsupported_d256(dev):
+    spec = workloads.small_spec("long_d256", seed=970, contexts=[300], queries=[100],
+                                head_dim=256, decode_layout=False)
     b = workloads.generate(spec, dev)
     with pytest.raises(pa.PAError) as e:
         run_prefill(b, torch.bfloat16)
