@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_decode.hip", "pa_reduce.hip", "pa_prefill.hip", "pa_verify.hip", "pa_append.hip",
+SOURCES = ["pa_decode.hip", "pa_reduce.hip", "pa_prefill.hip", "pa_verify.hip",
+           "pa_verify_d64.hip", "pa_verify_d128.hip", "pa_verify_d256.hip", "pa_append.hip",
            "pa_api.cpp"]
 ARCH = "gfx950"
 

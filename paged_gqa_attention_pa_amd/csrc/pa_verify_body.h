@@ -70,18 +70,20 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   constexpr int NV = D / 32;   // 16-byte V loads per lane and tile
   constexpr int CH = D / 8;    // 16-byte chunks per V row
   constexpr int kVRow = v_row<D>();
-  // Four row blocks: the wavefronts pair up; both of a pair stream the same
-  // tiles (the second read of a tile is an L2 hit) and each keeps two of the
-  // row blocks, so its registers are those of two row blocks.
-  constexpr bool kPairs = RB >= 4;
-  constexpr int RBW = kPairs ? RB / 2 : RB;  // row blocks of one wavefront
-  constexpr int WS = kPairs ? W / 2 : W;     // tile streams of the workgroup
+  // Four or eight row blocks: RB / 2 wavefronts share one stream of tiles
+  // (the later reads of a tile are L2 hits) and each keeps two of the row
+  // blocks, so its registers are those of two row blocks.
+  constexpr int WPS = RB >= 4 ? RB / 2 : 1;  // wavefronts per tile stream
+  static_assert(W % WPS == 0, "row blocks per workgroup");
+  constexpr bool kPairs = WPS > 1;
+  constexpr int RBW = RB / WPS;  // row blocks of one wavefront
+  constexpr int WS = W / WPS;    // tile streams of the workgroup
   // tiles per wavefront ring (registers bound it)
   constexpr int DEPTH = (RBW >= 2 || D >= 256) ? 2 : 3;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const int strm = kPairs ? wave >> 1 : wave;  // this wavefront's tile stream
-  const int rb0 = kPairs ? (wave & 1) * RBW : 0;  // its first row block
+  const int strm = wave / WPS;           // this wavefront's tile stream
+  const int rb0 = (wave % WPS) * RBW;    // its first row block
   const int lane = tid & 63;
   const int c = lane >> 4;
   const int n = lane & 15;

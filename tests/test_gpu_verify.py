@@ -185,3 +185,31 @@ def test_g32_prefill(dev, name, ctx, ql, out_dtype):
     b = workloads.generate(spec, dev)
     out, lse = run_prefill(b, out_dtype)
     compare(b, out, lse, label=f"prefill G=32 {name}")
+
+
+# one case per (G, row blocks) the short-run path builds at head dim 128, and
+# one just past it (128 rows: the query tiles)
+ROW_BLOCK_CASES = [(g, q) for g, qs in [(1, [2, 20, 40, 100]), (2, [2, 12, 24, 60]),
+                                        (4, [2, 8, 16, 32]), (8, [2, 4, 8, 16]),
+                                        (16, [2, 4, 8]), (32, [2, 4])] for q in qs]
+
+
+@pytest.mark.parametrize("g,q", ROW_BLOCK_CASES, ids=[f"G{g}_q{q}" for g, q in ROW_BLOCK_CASES])
+def test_verify_every_row_block(dev, g, q):
+    """Runs of q tokens x G heads = 16, 32 or 64 rows per unit (one, two or
+    four row blocks; four share a tile stream between two wavefronts), and
+    128 rows (query tiles), in fp32 and bf16."""
+    hkv = 1 if g == 32 else 8 // min(g, 8) if g > 8 else 2
+    hq = g * hkv
+    log(f"[verify G={g} q={q} Hq={hq} Hkv={hkv}]")
+    spec = workloads.small_spec(f"rb_g{g}_q{q}", seed=1100 + g + q, contexts=[q + 300, q + 5, 2000, q],
+                                queries=[q, max(1, q // 2), 1, q], num_q_heads=hq,
+                                num_kv_heads=hkv, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                         b.max_context_len, b.max_query_len)
+    tiles, _ = pa.select_tiles(pb)
+    assert tiles.kv_tile == (16 if q * g <= 64 else 32), "unexpected path"
+    for dt in (torch.float32, torch.bfloat16):
+        out, lse = run_prefill(b, dt)
+        compare(b, out, lse, label=f"verify G={g} q={q} {dt}")
