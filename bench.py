@@ -38,22 +38,22 @@ DECODE_BYTES_PER_TOKEN = 4096
 TRAFFIC = {
     # decode_kernel<4,8,false> + splitkv_reduce_kernel, num_splits 32
     # (profiles/decode_ctx32k_hbm_counters.md)
-    "decode_ctx32k": 135737957,
+    "decode_ctx32k": 135761419,
 }
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {
-    # unified_kernel<4,false> (profiles/prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 185374421,
-    # unified_kernel<4,false> + splitkv_reduce_kernel (profiles/mixed_unified_kernel_trace.md)
-    "mixed_unified": 643105086,
-    # verify_kernel<4,1,false> + unit_merge_kernel (profiles/spec_verify_b64_kernel_trace.md)
-    "spec_verify_b64": 1204251891,
+    # unified_kernel<4,false,128> (profiles/prefill_chunk2048_hbm_counters.md)
+    "prefill_chunk2048": 185094406,
+    # unified_kernel<4,false,128> + splitkv_reduce_kernel (profiles/mixed_unified_kernel_trace.md)
+    "mixed_unified": 643109880,
+    # verify_kernel<4,1,false,128> + unit_merge_kernel (profiles/spec_verify_b64_kernel_trace.md)
+    "spec_verify_b64": 1204187601,
 }
 
 # The same for one pa_cache_append call.
 APPEND_TRAFFIC = {
     # append_kernel (profiles/append_prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 67206455,
+    "prefill_chunk2048": 67203516,
 }
 
 
