@@ -53,7 +53,7 @@ PREFILL_TRAFFIC = {
 # The same for one pa_cache_append call.
 APPEND_TRAFFIC = {
     # append_kernel (profiles/append_prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 67203516,
+    "prefill_chunk2048": 67204233,
 }
 
 
@@ -104,6 +104,12 @@ def prefill_flops(b):
         # query i (0-based) of the chunk sees L - q + i + 1 keys
         total += q * (L - q) + q * (q + 1) // 2 if b.spec.causal else q * L
     return 4 * D * Hq * total
+
+
+def whole_replays(steps, per):
+    """Secondary lines time a whole number of multi-step replays: a replay of
+    a single step costs 5-10 us more on this stack (see --launch-study)."""
+    return -(-steps // per) * per
 
 
 def time_replays(torch, graph_all, singles, steps, warmup):
@@ -210,7 +216,8 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
     with torch.cuda.graph(g_all):
         for _ in range(per_replay):
             step()
-    total_ms, per = time_replays(torch, g_all, [g] * per_replay, steps, warmup)
+    total_ms, per = time_replays(torch, g_all, [g] * per_replay, whole_replays(steps, per_replay),
+                                 warmup)
     flops = prefill_flops(b)
     nbytes = prefill_bytes(b)
     avg_ms = sum(per) / len(per)
@@ -268,7 +275,7 @@ def bench_append(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk20
     with torch.cuda.graph(g_all):
         for st in sets:
             step(*st)
-    total_ms, per = time_replays(torch, g_all, singles, steps, warmup)
+    total_ms, per = time_replays(torch, g_all, singles, whole_replays(steps, len(singles)), warmup)
     avg_ms = sum(per) / len(per)
     nbytes = append_bytes(b)
     gbs = nbytes / (avg_ms * 1e-3) / 1e9

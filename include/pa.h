@@ -222,8 +222,10 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
  * query_start_loc order; query_start_loc NULL means one token per sequence
  * (T = num_seqs, decode).  T = problem->total_query_tokens.  k_pool,
  * v_pool: the caller's paged pools, written only at those slots.  Every
- * block-table entry a token lands in must be a valid page; a sequence with
- * context_lens[s] < q_len(s) is undefined (its tokens are skipped).
+ * block-table entry a token lands in must be a valid page of the pools; a
+ * sequence with context_lens[s] < q_len(s) is undefined.  Rows past their
+ * sequence's tokens, positions past the table row and negative table entries
+ * write nothing.
  * Pointers to bf16 data must be 16-byte aligned.  Host checks as for the
  * other calls; nothing is allocated. */
 pa_status pa_cache_append(const pa_problem* problem, const void* k_new, const void* v_new,

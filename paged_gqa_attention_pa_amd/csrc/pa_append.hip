@@ -46,8 +46,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
   }
   const int L = p.context_lens[s];
   const int pos = L - qlen + i;
-  if (pos < 0 || pos / kPage >= p.max_blocks) return;  // undefined input: skip
+  // Undefined input (a row past the sequence's tokens, a context shorter than
+  // its new tokens, a position past the table row, a padded table entry):
+  // nothing is written, so a bad batch cannot write outside the pools.
+  if (i >= qlen || pos < 0 || pos / kPage >= p.max_blocks) return;
   const int64_t page = p.block_tables[(int64_t)s * p.max_blocks + pos / kPage];
+  if (page < 0) return;
   const int64_t dst = page * p.stride_page + (int64_t)(pos % kPage) * p.stride_token +
                       (int64_t)h * p.stride_head + 8 * dc;
   const int64_t src = row * D + 8 * dc;
