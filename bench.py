@@ -47,7 +47,7 @@ PREFILL_TRAFFIC = {
     # unified_kernel<4,false,128> + splitkv_reduce_kernel (profiles/mixed_unified_kernel_trace.md)
     "mixed_unified": 643109880,
     # verify_kernel<4,1,false,128> + unit_merge_kernel (profiles/spec_verify_b64_kernel_trace.md)
-    "spec_verify_b64": 1204187601,
+    "spec_verify_b64": 1203505088,
 }
 
 # The same for one pa_cache_append call.

@@ -249,12 +249,13 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     t.num_splits = dc.splits;
     t.variant = dc.variant;
   } else if (verify_path(problem)) {
-    // short query runs: the decode grid choice, each unit one Q-block of
-    // max_query_len tokens x G heads, 4 wavefronts, even-work grid
+    // short query runs: each unit one Q-block of max_query_len tokens x G
+    // heads, 4 wavefronts, even-work grid, the short-run split bound
     t.kv_tile = pa::kDecodeTile;
     t.waves_per_wg = 4;
     t.q_tokens_per_tile = problem->max_query_len > 1 ? problem->max_query_len : 1;
-    t.num_splits = dc.splits;
+    t.num_splits = pa::table_short_splits(problem->num_seqs, problem->num_kv_heads,
+                                          problem->max_context_len, dc.splits);
     t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
                 pa::kVariantSeparateMerge | pa::kVariantEvenWork;
     t.tile_splits = 0;

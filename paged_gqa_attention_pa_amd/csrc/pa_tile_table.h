@@ -113,6 +113,21 @@ inline DecodeChoice table_decode(int num_seqs, int num_kv_heads, int max_context
   return c;
 }
 
+// Short query runs (one Q-block per (sequence, kv head) unit): the swept split
+// bound for the (units, context-bound) bucket when there is one, else the
+// decode choice, whose grid it shares.
+inline int table_short_splits(int num_seqs, int num_kv_heads, int max_context_len,
+                              int decode_splits) {
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  constexpr int kLast = sizeof(gen::kShortUnitBuckets) / sizeof(int) - 1;
+  const int ui = units > 2 * gen::kShortUnitBuckets[kLast]
+                     ? -1
+                     : bucket_floor(gen::kShortUnitBuckets, units);
+  const int ci = bucket_of(gen::kShortCtxBuckets, max_context_len);
+  if (ui >= 0 && ci >= 0 && gen::kShortSplits[ui][ci] > 0) return gen::kShortSplits[ui][ci];
+  return decode_splits;
+}
+
 // Prefill tile_splits for a batch without single-token sequences.
 inline int table_prefill_splits(int64_t total_query_tokens, int q_tile, int num_kv_heads,
                                  int max_context_len) {

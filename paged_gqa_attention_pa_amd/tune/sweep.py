@@ -13,7 +13,11 @@ times each candidate (num_splits, waves per workgroup, grid variant) on two
 length mixes, all contexts equal to the bound and contexts drawn uniformly in
 [bound/16, bound], and keeps the candidate with the least summed time relative
 to each mix's best.  Prefill: for query-tile workgroup counts and context
-bounds it times tile_splits in {1, 2, 4, 8} on prefill-only batches.
+bounds it times tile_splits in {1, 2, 4, 8} on prefill-only batches.  Short
+query runs (speculative-decode verification, and decode at G = 32 or head dims
+other than 128, which run on the same kernel): for (units, context bound)
+buckets it times the split bound on several (G, head dim, tokens) shapes and
+keeps the one with the least worst relative time over shapes and mixes.
 
 Timing: CUDA graphs of one call per K/V pool copy (copies rotate so the
 256 MiB Infinity Cache does not serve the pools), HIP events around replays,
@@ -40,6 +44,12 @@ VARIANTS = [2, 6]      # static grid + separate merge, even-work grid + separate
 PF_WG_BUCKETS = [16, 32, 64, 128, 256, 512, 1024]  # query-tile workgroups (tiles x Hkv)
 PF_CTX_BUCKETS = [1024, 4096, 16384, 65536]
 PF_TILE_SPLITS = [1, 2, 4, 8]
+# Short query runs (one Q-block per (sequence, kv head) unit on the even-work
+# grid): (G, head dim, query tokens) shapes swept for the split bound.
+SHORT_SHAPES = [(4, 128, 4), (8, 128, 4), (4, 64, 1), (4, 256, 1), (32, 128, 1)]
+SHORT_SPLITS = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+SHORT_UNIT_BUCKETS = [1, 8, 64, 512]
+SHORT_CTX_BUCKETS = [1024, 4096, 16384, 32768, 131072]
 
 
 def log(msg):
@@ -161,6 +171,68 @@ def sweep_prefill(torch, pa, workloads, dev, results):
             torch.cuda.empty_cache()
 
 
+def _short_batch(workloads, name, contexts, q, G, D, seed, dev, slack=2.5):
+    hkv = 1 if G == 32 else 8
+    used = sum(-(-c // 16) for c in contexts)
+    spec = workloads.WorkloadSpec(name=name, seed=seed, pool_pages=int(used * slack) + 8,
+                                  fixed=[(c, q) for c in contexts], num_q_heads=G * hkv,
+                                  num_kv_heads=hkv, head_dim=D, decode_layout=(q == 1),
+                                  max_blocks=max(1, -(-max(contexts) // 16)))
+    return spec, workloads.generate(spec, dev, fill="zero")
+
+
+def sweep_short(torch, pa, workloads, dev, results):
+    res = results.setdefault("short", {})
+    for G, D, q in SHORT_SHAPES:
+        shape = f"g{G}_d{D}_q{q}"
+        per_shape = res.setdefault(shape, {})
+        hkv = 1 if G == 32 else 8
+        for units in SHORT_UNIT_BUCKETS:
+            if units < hkv:
+                continue
+            B = units // hkv
+            for ctx in SHORT_CTX_BUCKETS:
+                if B * ctx * hkv * D > MAX_TOKENS * 8 * 128:
+                    continue
+                key = f"{units}x{ctx}"
+                if key in per_shape:
+                    continue
+                g = torch.Generator().manual_seed(units * 137 + ctx + G + D + q)
+                mixes = {"equal": [ctx] * B}
+                varied = torch.randint(max(q, ctx // 16), ctx + 1, (B,), generator=g).tolist()
+                varied[0] = ctx
+                mixes["varied"] = varied
+                times = {}
+                for mix, contexts in mixes.items():
+                    spec, b = _short_batch(workloads, f"sws_{shape}_{key}_{mix}", contexts, q, G,
+                                           D, 11, dev)
+                    pools = [(b.k_pool, b.v_pool), (b.k_pool.clone(), b.v_pool.clone())]
+                    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, B, spec.scale, ctx, q)
+                    out = torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)
+                    for S in SHORT_SPLITS:
+                        if S > 1 and S > max(1, -(-ctx // 16) // 4):
+                            continue
+                        t, _ = pa.select_tiles(pb)
+                        t.num_splits = S
+                        ws = torch.zeros(max(pa.workspace_size(pb, t), 256), dtype=torch.uint8,
+                                         device=dev)
+                        if q == 1:
+                            fns = [(lambda kp=kp, vp=vp, t=t, ws=ws: pa.decode(
+                                b.q, kp, vp, b.block_tables, b.context_lens, spec.scale, ctx,
+                                out=out, tiles=t, workspace=ws, problem=pb)) for kp, vp in pools]
+                        else:
+                            fns = [(lambda kp=kp, vp=vp, t=t, ws=ws: pa.prefill(
+                                b.q, b.query_start_loc, kp, vp, b.block_tables, b.context_lens,
+                                spec.scale, ctx, q, out=out, tiles=t, workspace=ws, problem=pb))
+                                for kp, vp in pools]
+                        times.setdefault(str(S), {})[mix] = round(_time_graph(torch, fns), 2)
+                    del b, pools
+                    torch.cuda.empty_cache()
+                per_shape[key] = times
+                best = min(times.items(), key=lambda kv: sum(kv[1].values()))
+                log(f"short {shape} units={units} ctx={ctx}: best S={best[0]} {best[1]}")
+
+
 NEAR_TIE = 1.02  # a candidate must beat the default by more than 2% to replace it
 
 
@@ -192,6 +264,33 @@ def choose(results):
     for key, times in results["prefill"].items():
         pf[key] = int(min(times, key=times.get))
     return dec, pf
+
+
+def choose_short(results):
+    """Per (units, context) bucket: the split bound whose worst time relative
+    to the best, over every swept short-run shape and both mixes, is least
+    (the smaller bound wins a near tie: fewer partials to merge)."""
+    rel = {}
+    for shape, buckets in results.get("short", {}).items():
+        for key, times in buckets.items():
+            best = {}
+            for S, per in times.items():
+                for mix, us in per.items():
+                    best[mix] = min(best.get(mix, 1e30), us)
+            for S, per in times.items():
+                r = max(per[m] / best[m] for m in per)
+                cur = rel.setdefault(key, {})
+                cur[S] = max(cur.get(S, 0.0), r)
+    out = {}
+    for key, scores in rel.items():
+        ordered = sorted(scores, key=lambda S: int(S))
+        c = min(ordered, key=scores.get)
+        for S in ordered:  # smallest bound within the tie margin
+            if scores[S] <= scores[c] * NEAR_TIE:
+                c = S
+                break
+        out[key] = int(c)
+    return out
 
 
 def emit_header(results, path=GEN_HEADER):
@@ -241,6 +340,21 @@ def emit_header(results, path=GEN_HEADER):
     for w in PF_WG_BUCKETS:
         row = [str(pf.get(f"{w}x{c}", 0)) for c in PF_CTX_BUCKETS]
         lines.append("    {" + ", ".join(row) + "},")
+    short = choose_short(results)
+    lines += [
+        "};",
+        "",
+        "// Short query runs: split bound per (units, context-bound) bucket, swept",
+        "// over (G, head dim, tokens) = " + ", ".join(f"({g}, {d}, {q})" for g, d, q in SHORT_SHAPES)
+        + ";",
+        "// 0 marks a shape not swept.",
+        f"constexpr int kShortUnitBuckets[] = {{{', '.join(map(str, SHORT_UNIT_BUCKETS))}}};",
+        f"constexpr int kShortCtxBuckets[] = {{{', '.join(map(str, SHORT_CTX_BUCKETS))}}};",
+        f"constexpr unsigned short kShortSplits[{len(SHORT_UNIT_BUCKETS)}][{len(SHORT_CTX_BUCKETS)}] = {{",
+    ]
+    for u in SHORT_UNIT_BUCKETS:
+        row = [str(short.get(f"{u}x{c}", 0)) for c in SHORT_CTX_BUCKETS]
+        lines.append("    {" + ", ".join(row) + "},")
     lines += ["};", "", "}  // namespace gen", "}  // namespace pa", ""]
     with open(path, "w") as f:
         f.write("\n".join(lines))
@@ -252,6 +366,8 @@ def main():
     ap.add_argument("--out-json", default=DEFAULT_JSON)
     ap.add_argument("--emit-only", action="store_true", help="regenerate the header from JSON")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-short", action="store_true")
     args = ap.parse_args()
     results = {"decode": {}, "prefill": {}}
     if os.path.exists(args.out_json):
@@ -268,9 +384,12 @@ def main():
         results["device"] = torch.cuda.get_device_name(0)
         t0 = time.time()
         try:
-            sweep_decode(torch, pa, workloads, dev, results)
+            if not args.no_decode:
+                sweep_decode(torch, pa, workloads, dev, results)
             if not args.no_prefill:
                 sweep_prefill(torch, pa, workloads, dev, results)
+            if not args.no_short:
+                sweep_short(torch, pa, workloads, dev, results)
         finally:
             with open(args.out_json, "w") as f:
                 json.dump(results, f, indent=0, sort_keys=True)

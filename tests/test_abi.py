@@ -148,6 +148,52 @@ def test_select_tiles_short_runs(lib):
     assert st == pa.PA_OK and t.kv_tile == 32
 
 
+def _gen_table(name):
+    """A constexpr array of the generated tile-table header, as nested lists."""
+    src = open(os.path.join(os.path.dirname(pa.__file__), "csrc", "pa_tile_table_gen.h")).read()
+    body = re.search(name + r"(?:\[\d*\])*\s*=\s*\{(.*?)\};", src, re.S).group(1)
+    rows = re.findall(r"\{([^{}]*)\}", body)
+    if not rows:
+        return [int(x) for x in body.split(",") if x.strip()]
+    return [[int(x) for x in r.split(",") if x.strip()] for r in rows]
+
+
+def test_short_run_split_table(lib):
+    """Short query runs take their split bound from the short-run table of
+    the generated header, by (units rounded down, context bound rounded up);
+    unswept buckets keep the decode choice."""
+    units_b = _gen_table("kShortUnitBuckets")
+    ctx_b = _gen_table("kShortCtxBuckets")
+    table = _gen_table("kShortSplits")
+    assert len(table) == len(units_b) and all(len(r) == len(ctx_b) for r in table)
+    checked = 0
+    for i, units in enumerate(units_b):
+        for j, ctx in enumerate(ctx_b):
+            blocks = -(-ctx // 16)
+            shapes = [dict(num_q_heads=32, num_kv_heads=1, num_seqs=units,
+                           total_query_tokens=units)]                       # G = 32 decode
+            if units >= 8:                                                  # G = 4, 4 tokens
+                shapes.append(dict(num_seqs=units // 8, max_query_len=4,
+                                   total_query_tokens=units // 2))
+            for kw in shapes:
+                pb = _problem(max_context_len=ctx, max_blocks_per_seq=blocks, **kw)
+                st, t, _ = _select(lib, pb)
+                assert st == pa.PA_OK, kw
+                if table[i][j] > 0:
+                    assert t.num_splits == table[i][j], (units, ctx, kw)
+                    checked += 1
+                # one unit more than the bucket, same context: same bucket
+                kw2 = dict(kw, num_seqs=kw["num_seqs"] + 1,
+                           total_query_tokens=kw["total_query_tokens"] + 1)
+                st, t2, _ = _select(lib, _problem(max_context_len=ctx, max_blocks_per_seq=blocks,
+                                                  **kw2))
+                next_floor = i + 1 < len(units_b) and (
+                    (kw2["num_seqs"] * kw2.get("num_kv_heads", 8)) >= units_b[i + 1])
+                if table[i][j] > 0 and not next_floor:
+                    assert t2.num_splits == table[i][j], (units, ctx, kw2)
+    assert checked > 0
+
+
 @pytest.mark.parametrize("ts", [-1, 9])
 def test_workspace_size_rejects_tile_splits(lib, ts):
     pb = _problem(max_query_len=64, total_query_tokens=256)

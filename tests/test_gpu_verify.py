@@ -166,6 +166,20 @@ def test_g32_decode(dev, splits, out_dtype):
     compare(b, out, lse, label=f"decode G=32 S={splits}")
 
 
+@pytest.mark.parametrize("ctx", [1025, 20000, 70000])
+@pytest.mark.parametrize("splits", [None, 256])
+def test_single_unit_many_splits(dev, ctx, splits):
+    """One sequence on one KV head (G = 32): the short-run table cuts the
+    only unit into up to 128 pieces, and 256 forced; every row checked."""
+    log(f"[single unit G=32 ctx={ctx} S={splits}]")
+    spec = workloads.small_spec("g32_one", seed=870 + ctx % 97, contexts=[ctx], queries=[1],
+                                num_q_heads=32, num_kv_heads=1)
+    b = workloads.generate(spec, dev)
+    for dt in (torch.bfloat16, torch.float32):
+        out, lse = run_decode(b, dt, splits)
+        compare(b, out, lse, label=f"single unit ctx={ctx} S={splits} {dt}")
+
+
 G32_PREFILL = [
     # (name, contexts, query lens): one-token rows, two-token runs (the
     # short-run kernel), chunks (query tiles of 8 tokens x 32 heads), a mix
