@@ -36,7 +36,11 @@
  *   query_start_loc int32 [B+1] (prefill): tokens of s are rows
  *                 [query_start_loc[s], query_start_loc[s+1]) of q and out.
  *   lse           fp32 [T, Hq], natural log of the softmax denominator
- *                 sum_j exp(scale * q.k_j); optional (NULL to skip).
+ *                 sum_j exp(scale * q.k_j); optional (NULL to skip).  When it
+ *                 is requested, kernels that round the weights P to bf16 for
+ *                 the P.V product carry them as bf16 high part + remainder
+ *                 instead (variant bit 0 below), so the LSE is not limited by
+ *                 bf16's 8-bit significand.
  *
  * Ownership and threading: every pointer is device memory owned by the
  * caller.  The compute calls never allocate, free or synchronise; they only
@@ -104,8 +108,9 @@ typedef struct pa_tiles {
   int32_t waves_per_wg;      /* wavefronts per workgroup                         */
   int32_t q_tokens_per_tile; /* query tokens per prefill workgroup               */
   int32_t variant;           /* bit 0 (prefill): carry P as a bf16 high part plus a  */
-                             /* bf16 remainder in P.V (relative weight error ~2^-18  */
-                             /* instead of ~2^-9); chosen for fp32 outputs.          */
+                             /* bf16 remainder in P.V (relative weight error <=     */
+                             /* 2^-16 instead of <= 2^-8); chosen for fp32 outputs, */
+                             /* and implied by a non-NULL lse.                       */
                              /* bit 1 (decode, S > 1): merge the splits in a second  */
                              /* kernel (pa_splitkv_reduce's) instead of in the last  */
                              /* workgroup of each sequence                           */

@@ -155,7 +155,9 @@ pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const voi
   const int S = tiles->num_splits;
   const int rb = pa::verify_row_blocks(G, problem->max_query_len > 1 ? problem->max_query_len : 1,
                                        problem->head_dim);
-  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
+  // an LSE is asked for: weights as bf16 high part + remainder, so its
+  // denominator is not rounded to bf16's 8-bit significand
+  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0 || lse != nullptr;
   pa::DecodeParams d;
   d.q = static_cast<const uint16_t*>(q);
   d.k_pool = static_cast<const uint16_t*>(k_pool);
@@ -477,7 +479,9 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.out_f32 = out_f32;
   d.causal = problem->causal;
 
-  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0;
+  // an LSE is asked for: weights as bf16 high part + remainder, so its
+  // denominator is not rounded to bf16's 8-bit significand
+  const bool precise = (tiles->variant & pa::kVariantPreciseP) != 0 || lse != nullptr;
   if (decode_only) {
     // every sequence is a decode row: the decode kernels alone (measured on a
     // batch of 64: 231 us against 267 us for the decode part of the unified
