@@ -1,12 +1,17 @@
 """Seeded random problems through pa_decode and pa_prefill against the fp64
 oracle: random query-head groups (G = 1..32), head dims (64, 128, 256),
 batch sizes, length mixes (empty sequences, single tokens, short runs,
-chunks on cached prefixes), causal or not, bf16 or fp32 outputs.  Each case
-goes through whatever kernels the host picks for it (decode kernels,
-short-run kernel, query tiles with or without decode workgroups, tile
-splits), so the routing is exercised on shapes no hand-written case names.
-Long rows are compared on a seeded sample of output rows.
+chunks on cached prefixes, a few past 32k keys), causal or not, bf16 or fp32 outputs, with or
+without the LSE, pools in the default layout or seen through other strides
+(head-major storage, or padded rows and heads holding NaN), and sometimes a
+forced split count over a NaN-filled workspace.  Each case goes through
+whatever kernels the host picks for it (decode kernels, short-run kernel,
+query tiles with or without decode workgroups, tile splits), so the routing
+is exercised on shapes no hand-written case names.  Long rows are compared
+on a seeded sample of output rows.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +21,7 @@ from test_gpu_parity import compare, dev, log, run_decode, run_prefill  # noqa: 
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 200
 MAX_ROWS = 384  # output rows checked per case (sampled beyond this)
 
 
@@ -40,7 +45,10 @@ def draw_case(i):
             q = 0
         else:
             q = int(rng.integers(17, 200))
-        prefix = 0 if q == 0 else int(rng.choice([0, rng.integers(0, 600), rng.integers(0, 3000)]))
+        # rarely past 32k keys, where the page-id window in LDS is restaged
+        prefix = 0 if q == 0 else int(rng.choice([0, rng.integers(0, 600), rng.integers(0, 3000),
+                                                  rng.integers(0, 3000),
+                                                  rng.integers(0, 3000) + 33000 * (i % 7 == 0)]))
         ctx.append(q + prefix)
         ql.append(q)
     if all(q == 0 for q in ql):
@@ -56,8 +64,27 @@ def draw_case(i):
     causal = bool(rng.integers(0, 4) > 0)
     out_dtype = torch.float32 if rng.integers(0, 3) == 0 else torch.bfloat16
     decode_layout = all(q == 1 for q in ql) and bool(rng.integers(0, 2))
+    layout = str(rng.choice(["default", "default", "head_major", "padded"]))
+    with_lse = bool(rng.integers(0, 3) > 0)
+    force = int(rng.choice([0, 0, 0, 2, 3, 8]))  # splits (decode) / tile splits (prefill)
     return dict(G=G, hkv=hkv, D=D, ctx=ctx, ql=ql, causal=causal, out_dtype=out_dtype,
-                decode_layout=decode_layout, seed=7100 + i)
+                decode_layout=decode_layout, layout=layout, with_lse=with_lse, force=force,
+                seed=7100 + i)
+
+
+def strided_pools(b, layout):
+    """The batch's pools seen through other strides, same logical contents."""
+    if layout == "head_major":
+        ks = b.k_pool.permute(0, 2, 1, 3).contiguous()
+        vs = b.v_pool.permute(0, 2, 1, 3).contiguous()
+        return ks.permute(0, 2, 1, 3), vs.permute(0, 2, 1, 3)
+    npg, P, Hkv, D = b.k_pool.shape
+    ks = torch.full((npg, P, Hkv + 1, D + 8), float("nan"), dtype=b.k_pool.dtype,
+                    device=b.k_pool.device)
+    vs = ks.clone()
+    ks[:, :, :Hkv, :D] = b.k_pool
+    vs[:, :, :Hkv, :D] = b.v_pool
+    return ks[:, :, :Hkv, :D], vs[:, :, :Hkv, :D]
 
 
 def expect_unsupported(c):
@@ -71,17 +98,25 @@ def expect_unsupported(c):
 def test_random_problem(dev, i):
     c = draw_case(i)
     log(f"[fuzz {i}] G={c['G']} Hkv={c['hkv']} D={c['D']} ctx={c['ctx']} q={c['ql']} "
-        f"causal={c['causal']} {c['out_dtype']} decode_layout={c['decode_layout']}")
+        f"causal={c['causal']} {c['out_dtype']} decode_layout={c['decode_layout']} "
+        f"layout={c['layout']} lse={c['with_lse']} force={c['force']}")
     spec = workloads.small_spec(f"fuzz{i}", c["seed"], c["ctx"], c["ql"],
                                 num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
                                 head_dim=c["D"], causal=c["causal"],
                                 decode_layout=c["decode_layout"])
     b = workloads.generate(spec, dev)
+    bg = b  # what the GPU sees; the oracle reads b's default layout
+    if c["layout"] != "default":
+        kv, vv = strided_pools(b, c["layout"])
+        bg = dataclasses.replace(b, k_pool=kv, v_pool=vv)
+    force = c["force"] or None
     try:
         if c["decode_layout"]:
-            out, lse = run_decode(b, c["out_dtype"])
+            out, lse = run_decode(bg, c["out_dtype"], splits=force, with_lse=c["with_lse"])
         else:
-            out, lse = run_prefill(b, c["out_dtype"])
+            out, lse = run_prefill(bg, c["out_dtype"], with_lse=c["with_lse"],
+                                   tile_splits=force if max(c["ql"]) > 1 else None,
+                                   stale_workspace=force is not None)
     except pa.PAError as e:
         assert e.status == pa.PA_ERR_UNSUPPORTED and expect_unsupported(c), str(e)
         return
