@@ -8,7 +8,8 @@ forced split count over a NaN-filled workspace.  Each case goes through
 whatever kernels the host picks for it (decode kernels, short-run kernel,
 query tiles with or without decode workgroups, tile splits), so the routing
 is exercised on shapes no hand-written case names.  Long rows are compared
-on a seeded sample of output rows.
+on a seeded sample of output rows.  The paged append gets the same random
+batches and pool layouts, compared bit for bit.
 """
 import dataclasses
 
@@ -16,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from paged_gqa_attention_pa_amd import pa, workloads
 from test_gpu_parity import compare, dev, log, run_decode, run_prefill  # noqa: F401
 
@@ -126,3 +128,52 @@ def test_random_problem(dev, i):
     if T > MAX_ROWS:
         rows = np.sort(np.random.default_rng(c["seed"]).choice(T, MAX_ROWS, replace=False))
     compare(b, out, lse, rows=rows, label=f"fuzz {i}")
+
+
+N_APPEND = 60
+
+
+def storage_pools(b, layout):
+    """(storage K, storage V, view K, view V, strides) for a pool layout:
+    the views are what the library is handed, the storage is what the
+    oracle reads through the same strides."""
+    if layout == "default":
+        return b.k_pool, b.v_pool, b.k_pool, b.v_pool, b.kv_strides()
+    npg, P, Hkv, D = b.k_pool.shape
+    if layout == "head_major":
+        ks = b.k_pool.permute(0, 2, 1, 3).contiguous()
+        vs = b.v_pool.permute(0, 2, 1, 3).contiguous()
+        kv, vv = ks.permute(0, 2, 1, 3), vs.permute(0, 2, 1, 3)
+    else:
+        ks = torch.full((npg, P, Hkv + 1, D + 8), float("nan"), dtype=b.k_pool.dtype,
+                        device=b.k_pool.device)
+        vs = ks.clone()
+        ks[:, :, :Hkv, :D] = b.k_pool
+        vs[:, :, :Hkv, :D] = b.v_pool
+        kv, vv = ks[:, :, :Hkv, :D], vs[:, :, :Hkv, :D]
+    return ks, vs, kv, vv, tuple(int(x) for x in kv.stride()[:3])
+
+
+@pytest.mark.parametrize("i", range(N_APPEND))
+def test_random_append(dev, i):
+    """pa_cache_append on random batches and pool layouts, bit for bit
+    against the oracle's append over the whole pool."""
+    c = draw_case(1000 + i)
+    log(f"[fuzz append {i}] Hkv={c['hkv']} D={c['D']} ctx={c['ctx']} q={c['ql']} "
+        f"decode_layout={c['decode_layout']} layout={c['layout']}")
+    spec = workloads.small_spec(f"fuzz_app{i}", c["seed"], c["ctx"], c["ql"],
+                                num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
+                                head_dim=c["D"], causal=c["causal"],
+                                decode_layout=c["decode_layout"])
+    b = workloads.generate(spec, dev)
+    kn, vn = workloads.new_kv(b, seed=c["seed"] + 1)
+    ks, vs, kv, vv, strides = storage_pools(b, c["layout"])
+    qsl = b.query_start_loc
+    k_exp, v_exp = oracle.append(
+        workloads.bf16_bits(ks), workloads.bf16_bits(vs), spec.page_size, strides,
+        workloads.bf16_bits(kn), workloads.bf16_bits(vn), b.block_tables.cpu().numpy(),
+        b.context_lens.cpu().numpy(), None if qsl is None else qsl.cpu().numpy())
+    pa.cache_append(kn, vn, kv, vv, b.block_tables, b.context_lens, qsl)
+    torch.cuda.synchronize()
+    assert np.array_equal(workloads.bf16_bits(ks), k_exp), "K pool differs from the oracle"
+    assert np.array_equal(workloads.bf16_bits(vs), v_exp), "V pool differs from the oracle"
