@@ -225,16 +225,21 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     // reach O through a zero weight
     const bool tail = (win0 + t + 1) * kKvTile > L;  // uniform
     const bool dead = tail && (win0 + t) * kKvTile + lkey >= L;
+    // element-wise copies: a whole-struct copy becomes a memcpy that can
+    // keep the staging registers in memory
+    const uint32_t keep = dead ? 0u : ~0u;
     if constexpr (kSplitKV) {
       if (stage_v)
         *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
-            dead ? make_uint4(0, 0, 0, 0) : r[0];
+            make_uint4(r[0].x & keep, r[0].y & keep, r[0].z & keep, r[0].w & keep);
       else
-        *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) = r[0];
+        *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) =
+            make_uint4(r[0].x, r[0].y, r[0].z, r[0].w);
     } else {
-      *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) = r[0];
+      *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) =
+          make_uint4(r[0].x, r[0].y, r[0].z, r[0].w);
       *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
-          dead ? make_uint4(0, 0, 0, 0) : r[1];
+          make_uint4(r[1].x & keep, r[1].y & keep, r[1].z & keep, r[1].w & keep);
     }
   };
   // Transposing V reads: lane (group gq = lane / 16, r = lane % 16) points
@@ -390,12 +395,15 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       for (int i = tid; i < nb; i += kThreads) pg_lds[i] = (b0 + i < nblk) ? bt[b0 + i] : 0;
       __syncthreads();
     }
-    uint4 rg[2];
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      load_tile(min(t, nw - 1), rg);
-      if (t < nw) store_tile(t, t, t, rg);
-    }
+    // the first three tiles' loads are all issued before any is stored, so
+    // the window start waits on memory once rather than three times
+    uint4 rg[2], r1[2], r2[2];
+    load_tile(0, rg);
+    load_tile(min(1, nw - 1), r1);
+    load_tile(min(2, nw - 1), r2);
+    store_tile(0, 0, 0, rg);
+    if (1 < nw) store_tile(1, 1, 1, r1);
+    if (2 < nw) store_tile(2, 2, 2, r2);
     load_tile(min(3, nw - 1), rg);
     __syncthreads();
     qk(0, st_cur);
