@@ -381,7 +381,9 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library is a "
-              "single-GPU kernel library; see DESIGN.md for how the path would shard.",
+              "single-GPU kernel library.  Attention shards across GPUs by KV head or by "
+              "sequence with no communication; very long contexts would shard by page range "
+              "and merge the (O, lse) partials with pa_splitkv_reduce after an all-gather.",
               file=sys.stderr)
         sys.exit(2)
     import torch
