@@ -322,12 +322,11 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       if constexpr (PRECISE) {
         psum += p0 + p1;
         pl[e >> 1] = pack_bf16x2(p0 - bf16lo(pk[e >> 1]), p1 - bf16hi(pk[e >> 1]));
-      } else {
-        // the row sum of the weights the MFMA uses (P rounded to bf16)
-        psum = add_bf16x2(pk[e >> 1], psum);
       }
     }
-    lsum += psum;
+    // (with P rounded to bf16, its row sum is taken in the MFMA phase that
+    // multiplies P by V, beside that phase's MFMAs: see pv)
+    if constexpr (PRECISE) lsum += psum;
   };
 
   // O^T += V^T P^T for the tile whose V is in buffer vbuf and whose P is in
@@ -337,6 +336,17 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // keeps sixteen hoisted addresses in registers and rebuilds each one every
   // tile).
   auto pv = [&](int vbuf) {
+    if constexpr (!PRECISE) {
+      // the row sum of the weights the MFMA uses (P rounded to bf16); it is
+      // added here, before the next tile's softmax can rescale lsum, so that
+      // its VALU work sits in the MFMA phase, where the SIMD has issue slots
+      // to spare, instead of lengthening the softmax phase
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) psum = add_bf16x2(pk[e], psum);
+      lsum += psum;
+      asm volatile("" : "+v"(lsum));  // keep the sum in this phase
+    }
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     lds_i16x4* vb = (lds_i16x4*)&v_lds[vbuf][vr_off];
     asm volatile("" : "+v"(vb));
