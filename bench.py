@@ -43,9 +43,9 @@ TRAFFIC = {
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {
     # unified_kernel<4,false,128> (profiles/prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 185083381,
+    "prefill_chunk2048": 184981238,
     # unified_kernel<4,false,128> + splitkv_reduce_kernel (profiles/mixed_unified_kernel_trace.md)
-    "mixed_unified": 643120681,
+    "mixed_unified": 643112747,
     # verify_kernel<4,1,false,128> + unit_merge_kernel (profiles/spec_verify_b64_kernel_trace.md)
     "spec_verify_b64": 1203505088,
 }
