@@ -55,7 +55,8 @@
  * returns PA_ERR_HIP.  Device-side data is trusted: a block-table entry
  * outside the pool, a context longer than max_context_len or than
  * max_blocks_per_seq*P, or a query length above max_query_len is undefined
- * behaviour.  Nothing aborts and no exception crosses the ABI.
+ * behaviour (pa_check_inputs reports each of these).  Nothing aborts and no
+ * exception crosses the ABI.
  */
 #ifndef PA_H
 #define PA_H
@@ -237,6 +238,36 @@ pa_status pa_cache_append(const pa_problem* problem, const void* k_new, const vo
                           const int32_t* query_start_loc, const int32_t* block_tables,
                           const int32_t* context_lens, void* k_pool, void* v_pool,
                           hipStream_t stream);
+
+/* Bits pa_check_inputs reports. */
+typedef enum {
+  PA_CHECK_PAGE = 1,           /* a block-table entry a context uses is outside [0, num_pages) */
+  PA_CHECK_CONTEXT_BOUND = 2,  /* context_lens[s] < 0 or > max_context_len                     */
+  PA_CHECK_CONTEXT_BLOCKS = 4, /* context_lens[s] > max_blocks_per_seq * page_size              */
+  PA_CHECK_QUERY_STARTS = 8,   /* query_start_loc not rising from 0 to total_query_tokens      */
+  PA_CHECK_QUERY_LEN = 16,     /* a query length above max_query_len                            */
+  PA_CHECK_CONTEXT_SHORT = 32  /* a sequence with more query tokens than context: its new
+                                  tokens have no positions.  Undefined for pa_cache_append
+                                  (which writes nothing for them); defined for attention, whose
+                                  rows before position 0 see no key (O = 0, lse = -inf), as a
+                                  decode row of an empty context does                          */
+} pa_check_flag;
+
+/* The compute calls trust the device-side tables and lengths: they only
+ * clamp, so that bad values cannot take them outside the block table or the
+ * workspace, and the results are then undefined.  This call checks them
+ * instead, for the problem a pa_decode, pa_prefill or pa_cache_append call
+ * would be given (the paged cache of the [IBM-PA] model-feature list:
+ * page = block_tables[s][t / P] for every token t < context_lens[s]).
+ * Enqueued on stream: *flags (device int32) is cleared, then gets the OR of
+ * the PA_CHECK_* bits of every failed check; the caller reads it after
+ * synchronising.  num_pages: pages in the K/V pools.  query_start_loc: as for
+ * pa_prefill, or NULL for one token per sequence.  block_tables and
+ * context_lens as for the compute calls.  Host arguments are checked first
+ * (PA_ERR_INVALID_ARG, nothing enqueued); nothing is allocated. */
+pa_status pa_check_inputs(const pa_problem* problem, int64_t num_pages,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start_loc, int32_t* flags, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* pa_status_string(pa_status status);

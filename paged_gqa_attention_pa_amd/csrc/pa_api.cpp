@@ -598,6 +598,29 @@ pa_status pa_cache_append(const pa_problem* problem, const void* k_new, const vo
   return from_hip(pa::launch_append(p, stream));
 }
 
+pa_status pa_check_inputs(const pa_problem* problem, int64_t num_pages,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start_loc, int32_t* flags, hipStream_t stream) {
+  pa_status st = check_problem(problem);
+  if (st != PA_OK) return st;
+  if (!block_tables || !context_lens || !flags || num_pages <= 0) return PA_ERR_INVALID_ARG;
+  if (!query_start_loc && problem->total_query_tokens != problem->num_seqs)
+    return PA_ERR_INVALID_ARG;  // one token per sequence
+  pa::CheckParams p;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start_loc = query_start_loc;
+  p.flags = flags;
+  p.num_pages = num_pages;
+  p.num_seqs = problem->num_seqs;
+  p.max_blocks = problem->max_blocks_per_seq;
+  p.max_context_len = problem->max_context_len;
+  p.max_query_len = query_start_loc ? problem->max_query_len : 1;
+  p.total_tokens = problem->total_query_tokens;
+  p.chunks = ceil_div(problem->max_blocks_per_seq, 256);
+  return from_hip(pa::launch_check(p, stream));
+}
+
 pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, int32_t rows,
                             int32_t num_splits, int32_t head_dim, void* out,
                             pa_dtype out_dtype, float* lse_out, hipStream_t stream) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 constexpr int kHeadDim = 128;   // built head dimension
@@ -131,6 +133,19 @@ hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int g
 // Workgroups of the unified prefill kernel that fit on the device at once.
 int unified_resident(int group, bool precise_p, int head_dim);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+
+// pa_check_inputs: device-side checks of the tables and lengths.
+struct CheckParams {
+  const int32_t* block_tables;     // [B, max_blocks]
+  const int32_t* context_lens;     // [B]
+  const int32_t* query_start_loc;  // [B+1] or null (one token per sequence)
+  int32_t* flags;                  // device int32, PA_CHECK_* bits
+  int64_t num_pages;
+  int32_t num_seqs, max_blocks, max_context_len, max_query_len, total_tokens;
+  int32_t chunks;                  // ceil(max_blocks / 256): workgroups per sequence
+};
+// Clears *flags, then ORs in the PA_CHECK_* bit of every failed check.
+hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 // Short-run path: merge the pieces of every (sequence, kv head) unit (rows
 // are (token, q head) pairs; piece_counts and context_lens are required,
 // query_start_loc null means one token per sequence); units = num_seqs *

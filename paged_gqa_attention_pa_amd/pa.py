@@ -19,7 +19,10 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = ra
 PA_BF16, PA_FP32 = 0, 1
 
 EXPORTED = ["pa_select_tiles", "pa_workspace_size", "pa_decode", "pa_prefill",
-            "pa_splitkv_reduce", "pa_cache_append", "pa_status_string"]
+            "pa_splitkv_reduce", "pa_cache_append", "pa_check_inputs", "pa_status_string"]
+# pa_check_inputs bits
+CHECK_PAGE, CHECK_CONTEXT_BOUND, CHECK_CONTEXT_BLOCKS = 1, 2, 4
+CHECK_QUERY_STARTS, CHECK_QUERY_LEN, CHECK_CONTEXT_SHORT = 8, 16, 32
 
 
 class Problem(ctypes.Structure):
@@ -70,6 +73,7 @@ def load() -> ctypes.CDLL:
         lib.pa_splitkv_reduce.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           P, ctypes.c_int32, P, P]
         lib.pa_cache_append.argtypes = [PP(Problem), P, P, P, P, P, P, P, P]
+        lib.pa_check_inputs.argtypes = [PP(Problem), ctypes.c_int64, P, P, P, P, P]
         for f in EXPORTED[:-1]:
             getattr(lib, f).restype = ctypes.c_int
         lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -336,3 +340,32 @@ def cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
     _check(lib.pa_cache_append(ctypes.byref(problem), _ptr(k_new), _ptr(v_new),
                                _ptr(query_start_loc), _ptr(block_tables), _ptr(context_lens),
                                _ptr(k_pool), _ptr(v_pool), _stream(dev)), "pa_cache_append")
+
+
+def check_inputs(problem: Problem, num_pages: int, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor,
+                 query_start_loc: Optional[torch.Tensor] = None) -> int:
+    """pa_check_inputs: the OR of the CHECK_* bits of every device-side check
+    that fails for this problem (0: tables and lengths are consistent).
+    Synchronises the current stream to read the result."""
+    lib = load()
+    dev = context_lens.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    for name, t in [("block_tables", block_tables), ("context_lens", context_lens),
+                    ("query_start_loc", query_start_loc)]:
+        if t is None:
+            continue
+        if t.device != dev or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous int32 on {dev}")
+    if block_tables.shape[0] != problem.num_seqs or context_lens.numel() != problem.num_seqs:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    if block_tables.shape[1] != problem.max_blocks_per_seq:
+        raise ValueError("block_tables row length must be max_blocks_per_seq")
+    if query_start_loc is not None and query_start_loc.numel() != problem.num_seqs + 1:
+        raise ValueError("query_start_loc needs num_seqs + 1 entries")
+    flags = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.pa_check_inputs(ctypes.byref(problem), int(num_pages), _ptr(block_tables),
+                               _ptr(context_lens), _ptr(query_start_loc), _ptr(flags),
+                               _stream(dev)), "pa_check_inputs")
+    return int(flags.item())

@@ -276,6 +276,22 @@ def test_cache_append_rejects_before_launch(lib):
     assert call(_problem(total_query_tokens=0), qsl=fake) == pa.PA_OK
 
 
+def test_check_inputs_rejects_before_launch(lib):
+    """pa_check_inputs validates its host arguments before enqueuing."""
+    pb = _problem()
+    fake = ctypes.c_void_p(0x10000)
+    nul = None
+    assert lib.pa_check_inputs(ctypes.byref(pb), 64, nul, fake, nul, fake, nul) == \
+        pa.PA_ERR_INVALID_ARG  # no block table
+    assert lib.pa_check_inputs(ctypes.byref(pb), 64, fake, fake, nul, nul, nul) == \
+        pa.PA_ERR_INVALID_ARG  # no flags word
+    assert lib.pa_check_inputs(ctypes.byref(pb), 0, fake, fake, nul, fake, nul) == \
+        pa.PA_ERR_INVALID_ARG  # empty pool
+    pp = _problem(max_query_len=64, total_query_tokens=256)
+    assert lib.pa_check_inputs(ctypes.byref(pp), 64, fake, fake, nul, fake, nul) == \
+        pa.PA_ERR_INVALID_ARG  # several tokens per sequence without query_start_loc
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert pa.status_string(s)
