@@ -119,6 +119,13 @@ typedef struct pa_tiles {
                              /* a fixed number of workgroups share all tiles of all */
                              /* sequences equally (cut at any tile, merged by lse);  */
                              /* a sequence is cut into at most S + 1 pieces          */
+                             /* bit 3 (one token per sequence, G <= 16): run the     */
+                             /* rows on the short-run kernel (pa_prefill's MFMA P.V  */
+                             /* path, even-work grid, workspace always needed) in    */
+                             /* place of the decode kernels; never the table's       */
+                             /* choice: on gfx950 it is within a few per cent of the */
+                             /* decode kernels on long batches either way and slower */
+                             /* on short ones                                        */
   int32_t tile_splits;       /* pa_prefill: each query tile's keys are cut into     */
                              /* this many runs of whole 32-key tiles (0 or 1: one   */
                              /* run, at most 8), merged by log-sum-exp; it spreads  */
@@ -157,7 +164,8 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
  * G = 32 (the decode kernels hold at most 16 query heads per KV head) runs
  * on the short-run kernel described at pa_prefill: one token of 32 heads is
  * a 32-row Q-block, the even-work grid always applies (waves_per_wg and the
- * merge bits are ignored) and the workspace is always needed. */
+ * merge bits are ignored) and the workspace is always needed; so does
+ * tiles->variant bit 3 at any G. */
 pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void* q,
                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
                     const int32_t* context_lens, void* out, float* lse, void* workspace,

@@ -103,6 +103,16 @@ int64_t short_run_rows(const pa_problem* pb) {
   return tokens * pb->num_q_heads;
 }
 
+// The short-run kernel serves this call: short query runs, decode at G = 32
+// or head dims other than 128, and decode batches whose launch shape asks
+// for it (variant bit 3).
+bool short_path(const pa_problem* pb, const pa_tiles* t) {
+  if (verify_path(pb)) return true;
+  const int G = pb->num_q_heads / pb->num_kv_heads;
+  return pb->max_query_len <= 1 && t && (t->variant & pa::kVariantShortDecode) != 0 &&
+         pa::verify_row_blocks(G, 1, pb->head_dim) > 0;
+}
+
 bool even_grid(const pa_tiles* t) {
   return t->num_splits > 1 && (t->variant & pa::kVariantEvenWork) != 0;
 }
@@ -111,7 +121,7 @@ Workspace workspace_layout(const pa_problem* pb, const pa_tiles* t) {
   Workspace w{0, 0, 0, 0, 0, 0, 0, 0};
   const int64_t D = pb->head_dim;
   const int S = t->num_splits;
-  const bool verify = verify_path(pb);
+  const bool verify = short_path(pb, t);
   if (S > 1 || verify) {
     // short query runs: (token, head) rows, always the even-work grid
     const int64_t rows = verify ? short_run_rows(pb) : (int64_t)pb->num_seqs * pb->num_q_heads;
@@ -311,7 +321,7 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
                            (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0) return PA_OK;
-  if (verify_path(problem))  // G = 32
+  if (short_path(problem, tiles))  // G = 32, head dims other than 128, or asked for
     return short_runs(problem, tiles, q, nullptr, k_pool, v_pool, block_tables, context_lens, out,
                       lse, static_cast<char*>(workspace), wl, stream);
 
@@ -406,7 +416,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
                        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
   if (problem->num_seqs == 0 || problem->total_query_tokens == 0) return PA_OK;
-  if (verify_path(problem))
+  if (short_path(problem, tiles))
     return short_runs(problem, tiles, q, query_start_loc, k_pool, v_pool, block_tables,
                       context_lens, out, lse, static_cast<char*>(workspace), wl, stream);
   const int qt = 256 / G;

@@ -20,6 +20,7 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kVariantPreciseP = 1;      // prefill: P as bf16 high + remainder
 constexpr int kVariantSeparateMerge = 2; // decode: merge splits in a second kernel
 constexpr int kVariantEvenWork = 4;      // decode: even-work grid (with the separate merge)
+constexpr int kVariantShortDecode = 8;   // decode: rows on the short-run kernel (even grid)
 
 struct DecodeParams {
   const uint16_t* q;        // [B, Hq, D] bf16

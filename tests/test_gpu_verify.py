@@ -147,6 +147,43 @@ def test_prefill_single_token_batch(dev, hq, hkv, variant, splits):
         compare(b, out, lse, label=f"single-token prefill G={hq // hkv} v{variant} S={splits} {dt}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 8), (16, 1)],
+                         ids=["g1", "g4", "g8", "g16"])
+@pytest.mark.parametrize("splits", [1, 4, 33])
+def test_decode_short_run_variant(dev, hq, hkv, splits):
+    """Variant bit 3 puts decode rows (G <= 16) on the short-run kernel, in
+    pa_decode and in a single-token pa_prefill; the workspace starts stale."""
+    log(f"[decode on the short-run kernel G={hq // hkv} S={splits}]")
+    ctx = [700, 33, 1, 0, 2049, 16, 4100]
+    spec = workloads.small_spec("dec_short", seed=880 + hq + splits, contexts=ctx,
+                                queries=[1] * len(ctx), num_q_heads=hq, num_kv_heads=hkv)
+    b = workloads.generate(spec, dev)
+    for dt in (torch.bfloat16, torch.float32):
+        pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                             b.max_context_len, 1, out_dtype=dt)
+        t, _ = pa.select_tiles(pb)
+        t.num_splits, t.waves_per_wg, t.variant = splits, 4, t.variant | 14
+        ws = torch.full((pa.workspace_size(pb, t),), 0xFF, dtype=torch.uint8, device=dev)
+        out, lse = run_decode(b, dt, splits, waves=4, variant=t.variant, workspace=ws)
+        compare(b, out, lse, label=f"short-run decode G={hq // hkv} S={splits} {dt}")
+    # the same rows through pa_prefill's packed layout
+    spec = workloads.small_spec("pre_short", seed=890 + hq + splits, contexts=ctx,
+                                queries=[1, 0, 1, 1, 1, 1, 1], num_q_heads=hq,
+                                num_kv_heads=hkv, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                         b.max_context_len, 1)
+    t, _ = pa.select_tiles(pb)
+    t.num_splits, t.waves_per_wg, t.variant = splits, 4, t.variant | 14
+    ws = torch.full((pa.workspace_size(pb, t),), 0xFF, dtype=torch.uint8, device=dev)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=dev)
+    out = pa.prefill(b.q, b.query_start_loc, b.k_pool, b.v_pool, b.block_tables,
+                     b.context_lens, spec.scale, b.max_context_len, 1, lse=lse, tiles=t,
+                     workspace=ws, problem=pb)
+    torch.cuda.synchronize()
+    compare(b, out, lse, label=f"short-run single-token prefill G={hq // hkv} S={splits}")
+
+
 # ---------------------------------------------------- 32 heads per KV head ----
 
 G32_DECODE = [1, 15, 16, 17, 300, 1000, 0, 2049]
