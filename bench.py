@@ -463,13 +463,16 @@ def main():
         note(f"append: {result['append']['us_per_step']} us, {result['append']['value']} GB/s")
     if args.all:
         others = {}
-        for name in ("decode_ctx512", "decode_b64"):
+        # pool copies cycled so the steps' K/V exceed the 256 MiB cache (8 GiB
+        # at batch 256 already does)
+        for name, pools in (("decode_ctx512", 6), ("decode_b64", 2), ("decode_b256_ctx8k", 1)):
             sub = argparse.Namespace(**{**vars(args), "workload": name, "splits": 0, "waves": 0,
-                                        "variant": -1, "pools": 2 if name == "decode_b64" else 6})
+                                        "variant": -1, "pools": pools})
             dd = bench_decode(torch, pa, workloads, sub, dev)
             ms = dd["total_ms"] / args.steps
-            others[name] = {"us_per_step": round(ms * 1e3, 2),
-                            "kv_gb_per_s": round(dd["nbytes"] / (ms * 1e-3) / 1e9, 1),
+            gbs = dd["nbytes"] / (ms * 1e-3) / 1e9
+            others[name] = {"us_per_step": round(ms * 1e3, 2), "kv_gb_per_s": round(gbs, 1),
+                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                             "num_splits": dd["tiles"].num_splits}
             note(f"{name}: {others[name]}")
             del dd

@@ -90,6 +90,11 @@ WORKLOADS = {
     "spec_verify_b64": WorkloadSpec(
         name="spec_verify_b64", seed=1006, pool_pages=40000, ctx_range=(128, 8192),
         num_draw=64, max_blocks=512, draw_query_len=4),
+    # large decode batch: 256 sequences of 8192 tokens (8 GiB of K/V), the
+    # steady-state streaming rate with no per-step start-up to amortise
+    "decode_b256_ctx8k": WorkloadSpec(
+        name="decode_b256_ctx8k", seed=1007, pool_pages=256 * 512 + 64,
+        fixed=[(8192, 1)] * 256, decode_layout=True),
 }
 WORKLOAD_ORDER = ["decode_ctx512", "decode_ctx32k", "decode_b64",
                   "prefill_chunk2048", "mixed_unified", "spec_verify_b64"]

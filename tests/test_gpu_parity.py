@@ -416,7 +416,7 @@ def _sample_rows(b, n, seed):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER + ["decode_b256_ctx8k"])
 def test_named_workload(dev, name):
     """Each workload at full size, launched as the benchmark launches it."""
     log(f"[workload {name}]")
@@ -425,6 +425,10 @@ def test_named_workload(dev, name):
     if spec.decode_layout:
         out, lse = run_decode(b, torch.bfloat16)
         rows = None
+        if b.num_seqs > 64:  # 8192 rows of 8192 keys: a seeded sample, the first and last rows
+            rng = np.random.default_rng(3)
+            n = b.num_seqs * spec.num_q_heads
+            rows = np.union1d(rng.choice(n, 480, replace=False), [0, 1, n - 2, n - 1])
     else:
         out, lse = run_prefill(b, torch.bfloat16)
         rows = _sample_rows(b, 3000, seed=1)
