@@ -148,6 +148,23 @@ def test_select_tiles_short_runs(lib):
     assert st == pa.PA_OK and t.kv_tile == 32
 
 
+def test_short_run_decode_variant_workspace(lib):
+    """Variant bit 3 moves decode rows (G <= 16) to the short-run kernel: the
+    table never sets it, and with it the workspace is needed even at S = 1
+    (S + 1 slots per row plus the piece counts)."""
+    pb = _problem()
+    st, t, _ = _select(lib, pb)
+    assert st == pa.PA_OK and (t.variant & 8) == 0
+    for S in (1, 4):
+        t1 = pa.Tiles(16, S, 4, 1, 14)
+        ws = ctypes.c_size_t(0)
+        assert lib.pa_workspace_size(ctypes.byref(pb), ctypes.byref(t1), ctypes.byref(ws)) == pa.PA_OK
+        assert ws.value >= pb.num_seqs * pb.num_q_heads * (S + 1) * 129 * 4
+        fake = ctypes.c_void_p(0x10000)  # never dereferenced: the workspace check fails first
+        assert lib.pa_decode(ctypes.byref(pb), ctypes.byref(t1), fake, fake, fake, fake, fake,
+                             fake, None, None, 0, None) == pa.PA_ERR_WORKSPACE
+
+
 def _gen_table(name):
     """A constexpr array of the generated tile-table header, as nested lists."""
     src = open(os.path.join(os.path.dirname(pa.__file__), "csrc", "pa_tile_table_gen.h")).read()
