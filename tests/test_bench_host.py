@@ -1,0 +1,52 @@
+"""bench.py's host-side figures on the CPU: the algorithmic FLOP and byte
+counts that its roofline fractions divide by, checked against brute-force
+counts over the mask, and the one-GPU guard (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+from paged_gqa_attention_pa_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _allowed_pairs(L, q, causal):
+    """Count (query, key) pairs the mask lets through by enumerating them:
+    query i of a run of q sits at position L - q + i and sees key j when
+    j < L and, if causal, j <= L - q + i."""
+    keys = np.arange(L)
+    n = 0
+    for i in range(q):
+        ok = keys < L
+        if causal:
+            ok &= keys <= L - q + i
+        n += int(ok.sum())
+    return n
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_prefill_flops_brute_force(causal):
+    spec = workloads.small_spec("flops", seed=5, contexts=[300, 77, 1, 0, 64, 40],
+                                queries=[140, 77, 1, 0, 3, 1], causal=causal)
+    b = workloads.generate(spec)
+    pairs = sum(_allowed_pairs(L, q, causal)
+                for L, q in zip(b.context_lens.tolist(), b.query_lens))
+    assert bench.prefill_flops(b) == 4 * spec.head_dim * spec.num_q_heads * pairs
+
+
+def test_decode_bytes_per_token():
+    """K and V rows of every KV head, bf16: 2 * Hkv * D * 2 bytes per token."""
+    for name in ("decode_ctx512", "decode_ctx32k", "decode_b64", "decode_b256_ctx8k"):
+        spec = workloads.WORKLOADS[name]
+        assert bench.DECODE_BYTES_PER_TOKEN == 2 * spec.num_kv_heads * spec.head_dim * 2
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
