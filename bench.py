@@ -39,9 +39,9 @@ TRAFFIC = {
     # decode_kernel<4,8,false> + splitkv_reduce_kernel, num_splits 32
     # (profiles/decode_ctx32k_hbm_counters.md)
     "decode_ctx32k": 135761419,
-    # decode_even_kernel<4,4> + splitkv_reduce_kernel, num_splits 128
+    # decode_even_kernel<4,4> + unit_merge_kernel, num_splits 128
     # (profiles/decode_b256_ctx8k_kernel_trace.md)
-    "decode_b256_ctx8k": 8605244566,
+    "decode_b256_ctx8k": 8604723335,
 }
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {

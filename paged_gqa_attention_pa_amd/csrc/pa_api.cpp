@@ -384,7 +384,11 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
     r.context_lens = context_lens;
     r.group = G;
     r.unit_rows = 0;
-    st = from_hip(pa::launch_reduce(r, stream));
+    // even grid: merge per (sequence, kv head) unit, its G rows in one
+    // workgroup, the piece count read once
+    st = from_hip(even ? pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, G,
+                                               stream)
+                       : pa::launch_reduce(r, stream));
   }
   return st;
 }
@@ -571,7 +575,11 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     r.context_lens = context_lens;
     r.group = G;
     r.unit_rows = 0;
-    st = from_hip(pa::launch_reduce(r, stream));
+    // even grid: merge per (sequence, kv head) unit, its G rows in one
+    // workgroup, the piece count read once
+    st = from_hip(even ? pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, G,
+                                               stream)
+                       : pa::launch_reduce(r, stream));
   }
   return st;
 }
