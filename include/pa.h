@@ -113,8 +113,8 @@ typedef struct pa_tiles {
                              /* 2^-16 instead of <= 2^-8); chosen for fp32 outputs, */
                              /* and implied by a non-NULL lse.                       */
                              /* bit 1 (decode, S > 1): merge the splits in a second  */
-                             /* kernel (pa_splitkv_reduce's) instead of in the last  */
-                             /* workgroup of each sequence                           */
+                             /* kernel instead of in the last workgroup of each      */
+                             /* sequence                                             */
                              /* bit 2 (decode, S > 1, needs bit 1): even-work grid: */
                              /* a fixed number of workgroups share all tiles of all */
                              /* sequences equally (cut at any tile, merged by lse);  */
@@ -148,8 +148,9 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
  * each sequence is cut into S contiguous, page-aligned ranges processed by
  * different workgroups; their (normalised output, lse) partials go to the
  * workspace and are merged by log-sum-exp in the same call.
- * With tiles->variant bit 1 set (the table's choice) a second kernel, the
- * one behind pa_splitkv_reduce, merges them; with it clear the merge runs
+ * With tiles->variant bit 1 set (the table's choice) a second kernel merges
+ * them: the one behind pa_splitkv_reduce, or on the even-work grid a merge
+ * with one workgroup per (sequence, kv head); with it clear the merge runs
  * inside the same launch: the last workgroup of a (sequence, kv head) to
  * finish, found with an atomic arrival counter, merges that sequence's
  * partials, so the call is one kernel.
