@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: paged GQA attention on one MI355X.
 
-Default workload: long-context decode (batch 1, 32 query / 8 KV heads,
+Headline workload: long-context decode (batch 1, 32 query / 8 KV heads,
 head_dim 128, context 32768, page size 16, shuffled pages in a 4096-page
 pool, bf16) with split-KV and the log-sum-exp merge.  One step = one decode
 call (every stage of the path) for the whole batch, replayed from a HIP
@@ -10,13 +10,16 @@ together far larger than the 256 MiB Infinity Cache), so every step streams
 its KV bytes from HBM.
 
 Reported: decode KV GB/s = 4096 bytes per context token (8 KV heads x K and
-V x 128 x 2 bytes) x context tokens / step time.  Alongside: the roofline of
-the decode launch (HIP events around every replay, on the replay stream), a
-secondary prefill line (causal chunked prefill 4 x (1024 + 2048), TFLOP/s
-over the causally allowed pairs, 4*D flops per (query, key, head)), and the
-fp64 oracle timed on the host cores.
+V x 128 x 2 bytes) x context tokens / step time.  Alongside, under
+"configs", every workload of the five-config set, each timed the same way
+(graph replays, inputs rotated over copies that together exceed the
+Infinity Cache) with its own roofline: decode lines against 8 TB/s of HBM,
+the causal chunked prefill against the dense bf16 MFMA peak (TFLOP/s over
+the causally allowed pairs, 4*D flops per (query, key, head)), the mixed
+batch against whichever of the two bounds its bytes and flops make larger.
+Then the paged append, and the fp64 oracle timed on the host cores.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 60] [--warmup 10]
 """
 import argparse
 import json
@@ -90,8 +93,8 @@ def parse():
                     help="time one decode step eagerly, as one graph replay, and as one of "
                          "eight steps in a replay, per decode workload; print one JSON line")
     ap.add_argument("--all", action="store_true",
-                    help="also time the other workloads (decode_ctx512, decode_b64, "
-                         "mixed_unified) and report them under 'others'")
+                    help="also time the extra workloads (decode_b256_ctx8k, spec_verify_b64, "
+                         "the decode_b64 append) and report them under 'others'")
     return ap.parse_args()
 
 
@@ -184,6 +187,23 @@ def bench_decode(torch, pa, workloads, args, dev):
                 pool_bytes=sum(p[0].numel() * 2 * 2 for p in pools))
 
 
+def decode_line(torch, pa, workloads, args, dev):
+    """A decode workload as a secondary line: time per step, KV GB/s and its
+    HBM roofline."""
+    args = argparse.Namespace(**{**vars(args), "steps": whole_replays(args.steps, args.pools)})
+    dd = bench_decode(torch, pa, workloads, args, dev)
+    ms = dd["total_ms"] / args.steps
+    gbs = dd["nbytes"] / (ms * 1e-3) / 1e9
+    return {"workload": args.workload, "metric": "decode KV GB/s (4096 B per context token)",
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(ms * 1e3, 2),
+            "bytes_per_step": dd["nbytes"], "pool_copies": args.pools,
+            "rotated_mib": round(dd["pool_bytes"] / 2 ** 20, 1),
+            "tiles": dd["tiles"].as_dict(),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": TRAFFIC.get(args.workload)}}
+
+
 def prefill_bytes(b):
     """KV bytes the causal rows read (4096 per key) plus Q and O."""
     kv = 0
@@ -193,7 +213,29 @@ def prefill_bytes(b):
     return kv + qo
 
 
-def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2048"):
+def roofline(nbytes, flops, ms, traffic):
+    """Roofline of one step of `ms` milliseconds: bound by whichever of
+    bytes / HBM peak and flops / MFMA peak is the larger; achieved and peak
+    in that bound's unit, frac = achieved / peak (for the bound that sets
+    the ideal time this is the whole-launch fraction)."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFS * 1e12)
+    sec = ms * 1e-3
+    if t_hbm >= t_mfma:
+        a = nbytes / sec / 1e9
+        return {"bound": "hbm", "achieved": round(a, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic}
+    a = flops / sec / 1e12
+    return {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic}
+
+
+def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2048",
+                  copies=3):
+    """One pa_prefill call per step, four steps per graph replay.  Each step
+    reads a different copy of Q and of the pools and writes a different
+    output (`copies` of them, together larger than the 256 MiB Infinity
+    Cache), so no step finds its inputs in that cache."""
     spec = workloads.WORKLOADS[name]
     b = workloads.generate(spec, dev, fill="zero")
     max_ctx, max_q = b.max_context_len, b.max_query_len
@@ -201,41 +243,47 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
                               max_ctx, max_q, causal=spec.causal)
     tiles, ws = pa.select_tiles(problem)
     workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
-    out = torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)
+    sets = [(b.q, b.k_pool, b.v_pool, torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev))]
+    for _ in range(max(1, copies) - 1):
+        sets.append((b.q.clone(), b.k_pool.clone(), b.v_pool.clone(),
+                     torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev)))
 
-    def step():
-        pa.prefill(b.q, b.query_start_loc, b.k_pool, b.v_pool, b.block_tables, b.context_lens,
+    def step(q, kp, vp, out):
+        pa.prefill(q, b.query_start_loc, kp, vp, b.block_tables, b.context_lens,
                    spec.scale, max_ctx, max_q, causal=spec.causal,
                    out=out, tiles=tiles, workspace=workspace, problem=problem)
 
-    step()
+    for st in sets:
+        step(*st)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    # four steps per replay, back to back as a serving loop issues them
-    per_replay = 4
+    per_replay = 4  # back to back, as a serving loop issues them
+    singles = []
+    for i in range(per_replay):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(*sets[i % len(sets)])
+        singles.append(g)
     g_all = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_all):
-        for _ in range(per_replay):
-            step()
-    total_ms, per = time_replays(torch, g_all, [g] * per_replay, whole_replays(steps, per_replay),
-                                 warmup)
+        for i in range(per_replay):
+            step(*sets[i % len(sets)])
+    total_ms, per = time_replays(torch, g_all, singles, whole_replays(steps, per_replay), warmup)
     flops = prefill_flops(b)
     nbytes = prefill_bytes(b)
     avg_ms = sum(per) / len(per)
     tfs = flops / (avg_ms * 1e-3) / 1e12
     gbs = nbytes / (avg_ms * 1e-3) / 1e9
-    whole = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (avg_ms * 1e-3)
+    rl = roofline(nbytes, flops, avg_ms, PREFILL_TRAFFIC.get(name))
+    set_bytes = sum(t.numel() * t.element_size() for t in sets[0])
     return {"workload": name,
-            "metric": "prefill attention TFLOP/s (causal pairs, 4*D flop each)",
-            "value": round(tfs, 2), "unit": "TFLOP/s", "ms_per_step": round(avg_ms, 4),
-            "gb_per_s": round(gbs, 1), "whole_launch_roofline_frac": round(whole, 4),
-            "tiles": tiles.as_dict(),
-            "roofline": {"bound": "mfma", "achieved": round(tfs, 2),
-                         "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                         "traffic": PREFILL_TRAFFIC.get(name)}}
+            "metric": "attention TFLOP/s over causal pairs (4*D flop each) and GB/s of "
+                      "K/V + Q + O bytes",
+            "value": round(tfs, 2), "unit": "TFLOP/s", "us_per_step": round(avg_ms * 1e3, 2),
+            "ms_per_step": round(avg_ms, 4), "gb_per_s": round(gbs, 1),
+            "flops_per_step": flops, "bytes_per_step": nbytes,
+            "input_copies": len(sets),
+            "rotated_mib": round(len(sets) * set_bytes / 2 ** 20, 1),
+            "tiles": tiles.as_dict(), "roofline": rl}
 
 
 def append_bytes(b):
@@ -456,45 +504,55 @@ def main():
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
         },
     }
+    del d, b
+    torch.cuda.empty_cache()
     if not args.no_prefill:
-        result["prefill"] = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
-                                          max(8, args.warmup))
-        note(f"prefill: {result['prefill']['value']} TFLOP/s")
-    if not args.no_prefill:
+        # Every config of the five-config set, each with its own roofline.
+        # Pool copies per decode step: enough that the copies cycled exceed
+        # the 256 MiB Infinity Cache (64 pages x 2 pools x 32 KiB = 4 MiB per
+        # copy at context 512; one decode_b64 step already reads 1.09 GB).
+        configs = {}
+        for name, pools in (("decode_ctx512", 96), ("decode_ctx32k", args.pools),
+                            ("decode_b64", 2)):
+            if name == args.workload:
+                configs[name] = {"same_as": "headline"}
+                continue
+            sub = argparse.Namespace(**{**vars(args), "workload": name, "splits": 0, "waves": 0,
+                                        "variant": -1, "pools": pools})
+            configs[name] = decode_line(torch, pa, workloads, sub, dev)
+            note(f"{name}: {configs[name]['us_per_step']} us, {configs[name]['value']} GB/s")
+            torch.cuda.empty_cache()
+        for name, copies in (("prefill_chunk2048", 3), ("mixed_unified", 2)):
+            configs[name] = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
+                                          max(8, args.warmup), name=name, copies=copies)
+            c = configs[name]
+            note(f"{name}: {c['us_per_step']} us, {c['value']} TFLOP/s, {c['gb_per_s']} GB/s, "
+                 f"roofline {c['roofline']['bound']} {c['roofline']['frac']}")
+            torch.cuda.empty_cache()
+        result["configs"] = configs
         result["append"] = bench_append(torch, pa, workloads, dev, max(16, args.steps // 2),
                                         max(8, args.warmup))
         note(f"append: {result['append']['us_per_step']} us, {result['append']['value']} GB/s")
     if args.all:
         others = {}
-        # pool copies cycled so the steps' K/V exceed the 256 MiB cache (8 GiB
-        # at batch 256 already does)
-        for name, pools in (("decode_ctx512", 6), ("decode_b64", 2), ("decode_b256_ctx8k", 1)):
-            sub = argparse.Namespace(**{**vars(args), "workload": name, "splits": 0, "waves": 0,
-                                        "variant": -1, "pools": pools})
-            dd = bench_decode(torch, pa, workloads, sub, dev)
-            ms = dd["total_ms"] / args.steps
-            gbs = dd["nbytes"] / (ms * 1e-3) / 1e9
-            others[name] = {"us_per_step": round(ms * 1e3, 2), "kv_gb_per_s": round(gbs, 1),
-                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                            "num_splits": dd["tiles"].num_splits}
-            note(f"{name}: {others[name]}")
-            del dd
-        mixed = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
-                              max(8, args.warmup), name="mixed_unified")
-        others["mixed_unified"] = mixed
+        sub = argparse.Namespace(**{**vars(args), "workload": "decode_b256_ctx8k", "splits": 0,
+                                    "waves": 0, "variant": -1, "pools": 1})
+        others["decode_b256_ctx8k"] = decode_line(torch, pa, workloads, sub, dev)
+        note(f"decode_b256_ctx8k: {others['decode_b256_ctx8k']}")
+        torch.cuda.empty_cache()
         spec_v = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
-                               max(8, args.warmup), name="spec_verify_b64")
+                               max(8, args.warmup), name="spec_verify_b64", copies=2)
         others["spec_verify_b64"] = spec_v
-        note(f"spec_verify_b64: {spec_v['ms_per_step'] * 1e3:.1f} us, {spec_v['gb_per_s']} GB/s")
+        note(f"spec_verify_b64: {spec_v['us_per_step']} us, {spec_v['gb_per_s']} GB/s")
         app = bench_append(torch, pa, workloads, dev, max(16, args.steps // 2),
                            max(8, args.warmup), name="decode_b64", pool_copies=1)
         others["append_decode_b64"] = app
         note(f"append decode_b64: {app['us_per_step']} us")
-        note(f"mixed_unified: {mixed['ms_per_step'] * 1e3:.1f} us, {mixed['gb_per_s']} GB/s, "
-             f"{mixed['value']} TFLOP/s, whole-launch frac {mixed['whole_launch_roofline_frac']}")
         result["others"] = others
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(workloads, b, args.cpu_seconds)
+        spec = workloads.WORKLOADS[args.workload]
+        result["cpu_baseline"] = cpu_baseline(workloads, workloads.generate(spec, dev, "zero"),
+                                              args.cpu_seconds)
         note(f"cpu baseline: {result['cpu_baseline']}")
     calibrate_copy(torch, dev, args.calibrate_copy)
     print(json.dumps(result), flush=True)

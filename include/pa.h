@@ -47,8 +47,13 @@
  * enqueue kernels on the caller's stream, so they can be captured in a HIP
  * graph.  Lengths, tables and query_start_loc are read on the device only;
  * the grid depends only on host fields of pa_problem (a static launch grid,
- * [IBM-PA] five-step list, static-grid and graph steps).  The library has
- * no mutable global state.
+ * [IBM-PA] five-step list, static-grid and graph steps).  The library's
+ * only mutable global state is a cache of occupancy figures (compute units
+ * x resident workgroups per unit, for the kernels whose grid is sized to
+ * the chip), kept per device and keyed on the device of the call's stream;
+ * each entry is filled on first use with a relaxed atomic store, and
+ * concurrent first calls compute and store the same value.  The tile table
+ * is constant.
  *
  * Errors: every host-side argument is checked before anything is enqueued;
  * a failed check returns a status and enqueues nothing.  A failed launch

@@ -196,7 +196,7 @@ pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.scale_log2 = problem->scale * pa::kLog2eHost;
   d.out_f32 = problem->out_dtype == PA_FP32;
   d.causal = problem->causal;
-  const int nw = pa::verify_resident(G, rb, precise, problem->head_dim);
+  const int nw = pa::verify_resident(G, rb, precise, problem->head_dim, stream);
   if (nw <= 0) return PA_ERR_HIP;
   pa_status st = from_hip(pa::launch_verify(d, G, rb, precise, problem->head_dim, nw, stream));
   if (st != PA_OK) return st;
@@ -362,7 +362,7 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
   p.causal = problem->causal;
   const bool separate = S > 1 && (tiles->variant & pa::kVariantSeparateMerge) != 0;
   if (even) {
-    const int nw = pa::decode_even_resident(G, waves);
+    const int nw = pa::decode_even_resident(G, waves, stream);
     if (nw <= 0) return PA_ERR_HIP;
     if ((st = from_hip(pa::launch_decode_even(p, G, waves, nw, stream))) != PA_OK) return st;
   } else if ((st = from_hip(pa::launch_decode(p, G, waves, !separate, stream))) != PA_OK) {
@@ -505,7 +505,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
     if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
     if (even) {
-      const int nw = pa::decode_even_resident(G, waves);
+      const int nw = pa::decode_even_resident(G, waves, stream);
       if (nw <= 0) return PA_ERR_HIP;
       if ((st = from_hip(pa::launch_decode_even(d, G, waves, nw, stream))) != PA_OK) return st;
     } else if ((st = from_hip(pa::launch_decode(d, G, waves, false, stream))) != PA_OK) {
@@ -535,7 +535,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   const int64_t nx = (int64_t)ceil_div(problem->total_query_tokens, qt) + problem->num_seqs;
   int64_t n_dec = decode_rows ? (int64_t)problem->num_seqs * problem->num_kv_heads * S : 0;
   if (even) {
-    n_dec = pa::unified_resident(G, precise, problem->head_dim);
+    n_dec = pa::unified_resident(G, precise, problem->head_dim, stream);
     if (n_dec <= 0) return PA_ERR_HIP;
   }
   if (nx * problem->num_kv_heads * TS + n_dec > 0x7fffffff) return PA_ERR_UNSUPPORTED;
@@ -575,11 +575,11 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     r.context_lens = context_lens;
     r.group = G;
     r.unit_rows = 0;
-    // even grid: merge per (sequence, kv head) unit, its G rows in one
-    // workgroup, the piece count read once
-    st = from_hip(even ? pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, G,
-                                               stream)
-                       : pa::launch_reduce(r, stream));
+    // The decode workgroups write their partials at sequence rows b*Hq + h,
+    // and only single-token sequences own any: the per-row merge maps each
+    // such row to its token's output row and skips every other sequence
+    // before it reads a piece count (which may be stale for them).
+    st = from_hip(pa::launch_reduce(r, stream));
   }
   return st;
 }

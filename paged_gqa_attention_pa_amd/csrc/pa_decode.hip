@@ -65,12 +65,18 @@ const void* even_kernel(int group, int waves) {
 
 }  // namespace
 
-int decode_even_resident(int group, int waves) {
+int stream_device(hipStream_t stream) {
+  hipDevice_t dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return -1;
+  return (int)dev;
+}
+
+int decode_even_resident(int group, int waves, hipStream_t stream) {
   // per device and (group, waves): CUs x resident workgroups per CU
   constexpr int kDevs = 64;
   static std::atomic<int> cache[kDevs][5][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  const int dev = stream_device(stream);
+  if (dev < 0 || dev >= kDevs) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
   const int wi = waves == 8 ? 1 : 0;
   const int cached = cache[dev][gi][wi].load(std::memory_order_relaxed);

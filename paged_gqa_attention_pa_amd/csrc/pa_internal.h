@@ -125,14 +125,20 @@ hipError_t launch_decode(const DecodeParams& p, int group, int waves, bool fused
 // Even-work decode grid of nw workgroups (separate merge only).
 hipError_t launch_decode_even(const DecodeParams& p, int group, int waves, int nw,
                               hipStream_t stream);
-// Workgroups of the even-work decode kernel that fit on the device at once.
-int decode_even_resident(int group, int waves);
+// Device that work enqueued on `stream` runs on (the current device for the
+// null stream), or -1.  The occupancy figures below are cached per device,
+// keyed on it.
+int stream_device(hipStream_t stream);
+// Workgroups of the even-work decode kernel that fit at once on the device
+// of `stream`.
+int decode_even_resident(int group, int waves, hipStream_t stream);
 // Prefill tiles (nx x Hkv workgroups) and n_dec decode workgroups (split x
 // Hkv x B, for the single-token sequences of a mixed batch) in one launch.
 hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int group, int nx,
                           int n_dec, bool precise_p, int head_dim, hipStream_t stream);
-// Workgroups of the unified prefill kernel that fit on the device at once.
-int unified_resident(int group, bool precise_p, int head_dim);
+// Workgroups of the unified prefill kernel that fit at once on the device of
+// `stream`.
+int unified_resident(int group, bool precise_p, int head_dim, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 
 // pa_check_inputs: device-side checks of the tables and lengths.
@@ -158,7 +164,7 @@ hipError_t launch_unit_merge(const ReduceParams& p, int units, int unit_rows,
 // blocks per unit (1, 2 or 4; 0 when not built), resident workgroups of that
 // kernel, and the even-work launch of nw workgroups.
 int verify_row_blocks(int group, int max_query_len, int head_dim);
-int verify_resident(int group, int rb, bool precise_p, int head_dim);
+int verify_resident(int group, int rb, bool precise_p, int head_dim, hipStream_t stream);
 hipError_t launch_verify(const DecodeParams& p, int group, int rb, bool precise_p, int head_dim,
                          int nw, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

@@ -86,11 +86,11 @@ const void* unified_kernel_of(int group, bool precise, int head_dim) {
 
 }  // namespace
 
-int unified_resident(int group, bool precise_p, int head_dim) {
+int unified_resident(int group, bool precise_p, int head_dim, hipStream_t stream) {
   constexpr int kDevs = 64;
   static std::atomic<int> cache[kDevs][6][2][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  const int dev = stream_device(stream);
+  if (dev < 0 || dev >= kDevs) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : group == 16 ? 4 : 5;
   std::atomic<int>& slot = cache[dev][gi][precise_p ? 1 : 0][head_dim == 64 ? 0 : 1];
   const int cached = slot.load(std::memory_order_relaxed);

@@ -41,11 +41,11 @@ int verify_row_blocks(int group, int max_query_len, int head_dim) {
   return (head_dim > 128 && rb > 2) ? 0 : rb;
 }
 
-int verify_resident(int group, int rb, bool precise, int head_dim) {
+int verify_resident(int group, int rb, bool precise, int head_dim, hipStream_t stream) {
   constexpr int kDevs = 64;
   static std::atomic<int> cache[kDevs][6][4][2][3];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  const int dev = stream_device(stream);
+  if (dev < 0 || dev >= kDevs) return 0;
   std::atomic<int>& slot =
       cache[dev][group_index(group)][rb_index(rb)][precise ? 1 : 0][dim_index(head_dim)];
   const int cached = slot.load(std::memory_order_relaxed);

@@ -50,3 +50,19 @@ def test_more_than_one_gpu_is_refused():
                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_roofline_bound_follows_the_larger_ideal_time():
+    """A line is priced against the bound whose ideal time is larger, and its
+    fraction is that ideal time over the measured one."""
+    ms = 0.1
+    # HBM-heavy: 600 MB and 75 GFLOP (the mixed batch's proportions)
+    r = bench.roofline(600e6, 75e9, ms, None)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    ideal = max(600e6 / (bench.HBM_PEAK_GBS * 1e9), 75e9 / (bench.MFMA_BF16_PEAK_TFS * 1e12))
+    assert abs(r["frac"] - round(ideal / (ms * 1e-3), 4)) < 1e-9
+    # MFMA-heavy: 185 MB and 275 GFLOP (the chunked prefill's)
+    r = bench.roofline(185e6, 275e9, ms, 123)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["traffic"] == 123
+    ideal = 275e9 / (bench.MFMA_BF16_PEAK_TFS * 1e12)
+    assert abs(r["frac"] - round(ideal / (ms * 1e-3), 4)) < 1e-9

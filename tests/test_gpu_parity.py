@@ -1,10 +1,13 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Tolerances (per element): fp32 outputs 2e-3; bf16 outputs 1e-2, widened to
-one bf16 ulp of the reference (2^-7 |ref|) where that is larger (|ref| >
-1.28), since rounding an exact result to bf16 alone can err by half an ulp;
-the natural-log LSE 2e-3.  Indexing cases (dominant
-logit, page permutation, NaN-poisoned stale slots) must match bit for bit.
+Tolerances (per element): fp32 outputs 2e-3; bf16 outputs
+max(1e-2, h(ref) + 2^-8), where h(ref) = 2^(floor(log2 |ref|) - 8) is the
+half-ulp of bf16 at the reference value (what rounding the exact result to
+bf16 alone can cost) and 2^-8 the arithmetic budget of kernels that round
+the softmax weights to bf16 before the P.V product; the widening starts at
+|ref| >= 2, where the half-ulp (2^-7) leaves too little of 1e-2 for that
+budget.  The natural-log LSE: 2e-3.  Indexing cases (dominant logit, page
+permutation, NaN-poisoned stale slots) must match bit for bit.
 """
 import math
 import sys
@@ -58,10 +61,12 @@ def run_decode(b, out_dtype=torch.bfloat16, splits=None, with_lse=True, waves=No
 
 
 def run_prefill(b, out_dtype=torch.bfloat16, with_lse=True, tile_splits=None,
-                stale_workspace=False):
+                stale_workspace=False, splits=None, variant=None, workspace=None):
     """pa_prefill on a batch; tile_splits forces the query-tile split count,
-    stale_workspace fills the workspace with NaN first (pa_prefill needs no
-    zeroed counters: its decode rows always use the separate merge)."""
+    splits / variant the decode rows' split count and grid, stale_workspace
+    fills the workspace with NaN first (pa_prefill needs no zeroed counters:
+    its decode rows always use the separate merge); a given workspace is
+    used as it is."""
     lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device=b.q.device) if with_lse else None
     qsl = b.query_start_loc
     if qsl is None:
@@ -72,9 +77,14 @@ def run_prefill(b, out_dtype=torch.bfloat16, with_lse=True, tile_splits=None,
     tiles, _ = pa.select_tiles(pb)
     if tile_splits is not None:
         tiles.tile_splits = tile_splits
+    if splits is not None:
+        tiles.num_splits = splits
+    if variant is not None:
+        tiles.variant = variant
     ws = pa.workspace_size(pb, tiles)
-    workspace = None
-    if ws:
+    if workspace is not None:
+        assert workspace.numel() >= ws
+    elif ws:
         workspace = torch.zeros(ws, dtype=torch.uint8, device=b.q.device)
         if stale_workspace:
             workspace.fill_(0xFF)  # every fp32 slot reads as NaN
@@ -84,6 +94,15 @@ def run_prefill(b, out_dtype=torch.bfloat16, with_lse=True, tile_splits=None,
                      workspace=workspace, problem=pb)
     torch.cuda.synchronize()
     return out, lse
+
+
+def bf16_allowance(ref, tol=1e-2):
+    """Per-element bar for bf16 outputs: max(tol, half-ulp of bf16 at |ref|
+    + 2^-8).  Below |ref| = 2 this is the plain tol."""
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    half_ulp = np.where(a > 0, np.exp2(e - 8), 0.0)
+    return np.maximum(tol, half_ulp + 2.0 ** -8)
 
 
 def compare(b, out, lse, rows=None, label=""):
@@ -101,9 +120,9 @@ def compare(b, out, lse, rows=None, label=""):
     err = float(np.max(diff)) if got.size else 0.0
     log(f"{label}: rows={ref.shape[0]} max|err|={err:.3e} (tol {tol})")
     if out.dtype == torch.bfloat16:
-        allowed = np.maximum(tol, 2.0 ** -7 * np.abs(ref))
+        allowed = bf16_allowance(ref, tol)
         worst = float(np.max(diff - allowed)) if got.size else -1.0
-        assert worst <= 0, f"{label}: error exceeds max(1e-2, 1 bf16 ulp) by {worst}"
+        assert worst <= 0, f"{label}: error exceeds max(1e-2, half-ulp + 2^-8) by {worst}"
     else:
         assert err <= tol, f"{label}: max|err| {err} > {tol}"
     if got_lse is not None:
@@ -285,14 +304,72 @@ PREFILL_CASES = [
 
 
 @pytest.mark.parametrize("name,ctx,ql,causal", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
-@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_prefill_small(dev, name, ctx, ql, causal, out_dtype):
-    log(f"[prefill {name} {out_dtype}]")
+@pytest.mark.parametrize("out_dtype,with_lse", [(torch.bfloat16, True), (torch.float32, True),
+                                                (torch.bfloat16, False)],
+                         ids=["bf16", "f32", "bf16_nolse"])
+def test_prefill_small(dev, name, ctx, ql, causal, out_dtype, with_lse):
+    """bf16 output without an LSE is the launch the benchmark times: P
+    rounded to bf16, one P.V MFMA per step (the others carry P as bf16 high
+    part + remainder)."""
+    log(f"[prefill {name} {out_dtype} lse={with_lse}]")
     spec = workloads.small_spec(f"pre_{name}", seed=200 + sum(ql), contexts=ctx, queries=ql,
                                 causal=causal, decode_layout=False)
     b = workloads.generate(spec, dev)
-    out, lse = run_prefill(b, out_dtype)
-    compare(b, out, lse, label=f"prefill {name}")
+    out, lse = run_prefill(b, out_dtype, with_lse=with_lse)
+    compare(b, out, lse, label=f"prefill {name} lse={with_lse}")
+
+
+MIXED_EVEN_CASES = [
+    # (name, contexts, query lens): single-token sequences after, before and
+    # between prefill chunks, an empty context among them
+    ("decodes_last", [260, 513, 900, 40], [100, 200, 1, 1]),
+    ("decodes_first", [900, 40, 260, 513], [1, 1, 100, 200]),
+    ("interleaved", [2000, 300, 700, 1, 5000, 0], [1, 150, 1, 1, 64, 1]),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql", MIXED_EVEN_CASES, ids=[c[0] for c in MIXED_EVEN_CASES])
+@pytest.mark.parametrize("splits", [2, 8, 33])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_mixed_even_grid(dev, name, ctx, ql, splits, out_dtype):
+    """A mixed batch whose decode rows run on the even-work grid (variant
+    bits 1 and 2) with several splits, over a zero-filled workspace, every
+    row compared: the merge must read the decode rows' partials where the
+    decode workgroups wrote them (sequence rows) and leave prefill rows
+    alone."""
+    log(f"[mixed even grid {name} S={splits} {out_dtype}]")
+    spec = workloads.small_spec(f"mixeven_{name}", seed=900 + splits + sum(ql), contexts=ctx,
+                                queries=ql, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    variant = 6 | (1 if out_dtype == torch.float32 else 0)
+    out, lse = run_prefill(b, out_dtype, splits=splits, variant=variant)
+    compare(b, out, lse, label=f"mixed even {name} S={splits}")
+
+
+@pytest.mark.parametrize("splits", [4, 33])
+def test_mixed_after_decode_same_workspace(dev, splits):
+    """A decode-only call and then a mixed call share one workspace: the
+    piece counts the decode call left for units that are prefill chunks in
+    the mixed call must not reach the mixed call's output."""
+    log(f"[mixed after decode, shared workspace, S={splits}]")
+    dspec = workloads.small_spec("shared_dec", seed=950 + splits, contexts=[3000, 4000, 900, 40],
+                                 queries=[1, 1, 1, 1], decode_layout=False)
+    mspec = workloads.small_spec("shared_mix", seed=960 + splits, contexts=[260, 513, 900, 40],
+                                 queries=[100, 200, 1, 1], decode_layout=False)
+    bd = workloads.generate(dspec, dev)
+    bm = workloads.generate(mspec, dev)
+    sizes = []
+    for b in (bd, bm):
+        pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, b.spec.scale,
+                             b.max_context_len, max(b.max_query_len, 1), out_dtype=torch.float32)
+        t, _ = pa.select_tiles(pb)
+        t.num_splits, t.variant = splits, 7
+        sizes.append(pa.workspace_size(pb, t))
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=dev)
+    out_d, lse_d = run_prefill(bd, torch.float32, splits=splits, variant=7, workspace=ws)
+    compare(bd, out_d, lse_d, label=f"shared ws decode S={splits}")
+    out_m, lse_m = run_prefill(bm, torch.float32, splits=splits, variant=7, workspace=ws)
+    compare(bm, out_m, lse_m, label=f"shared ws mixed S={splits}")
 
 
 TILE_SPLIT_CASES = [
@@ -418,24 +495,35 @@ def _sample_rows(b, n, seed):
 
 @pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER + ["decode_b256_ctx8k"])
 def test_named_workload(dev, name):
-    """Each workload at full size, launched as the benchmark launches it."""
+    """Each workload at full size, launched as the benchmark launches it
+    (table launch shape, bf16 output, no LSE: for the query-tile and
+    short-run kernels that is the variant with P rounded to bf16), every
+    row compared with the oracle except at batch 256 (a seeded sample);
+    query-layout workloads are also run with an LSE (the precise variant) on
+    sampled rows."""
     log(f"[workload {name}]")
     spec = workloads.WORKLOADS[name]
     b = workloads.generate(spec, dev, fill="nan")
     if spec.decode_layout:
-        out, lse = run_decode(b, torch.bfloat16)
+        out, _ = run_decode(b, torch.bfloat16, with_lse=False)
         rows = None
         if b.num_seqs > 64:  # 8192 rows of 8192 keys: a seeded sample, the first and last rows
             rng = np.random.default_rng(3)
             n = b.num_seqs * spec.num_q_heads
             rows = np.union1d(rng.choice(n, 480, replace=False), [0, 1, n - 2, n - 1])
+        compare(b, out, None, rows=rows, label=f"workload {name}")
+        out, lse = run_decode(b, torch.bfloat16)
+        compare(b, out, lse, rows=rows, label=f"workload {name} with lse")
     else:
+        out, _ = run_prefill(b, torch.bfloat16, with_lse=False)
+        compare(b, out, None, label=f"workload {name} (benchmarked launch, all rows)")
+        del out
         out, lse = run_prefill(b, torch.bfloat16)
         rows = _sample_rows(b, 3000, seed=1)
         if name == "mixed_unified":  # every decode row too
             dec = np.arange(16 * 32, dtype=np.int64)
             rows = np.union1d(rows, dec)
-    compare(b, out, lse, rows=rows, label=f"workload {name}")
+        compare(b, out, lse, rows=rows, label=f"workload {name} with lse")
     if name == "decode_ctx512":
         out32, lse32 = run_decode(b, torch.float32)
         compare(b, out32, lse32, label="workload decode_ctx512 fp32")
