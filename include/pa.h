@@ -177,6 +177,37 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
                     const int32_t* context_lens, void* out, float* lse, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the scratch array behind pa_decode_noalloc, on each GPU. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split partials, piece counts and
+ * merge counters that pa_decode keeps in the caller's workspace live here in
+ * a file-scope device array of PA_NOALLOC_SCRATCH_BYTES (64 MiB), which the
+ * library holds on every GPU it runs on until the process ends.  Arguments,
+ * kernels and results are those of pa_decode; the caller still passes the
+ * inputs and outputs.
+ * Errors: as pa_decode, plus PA_ERR_WORKSPACE (nothing enqueued) when
+ * pa_workspace_size for this problem and launch shape exceeds
+ * PA_NOALLOC_SCRATCH_BYTES (e.g. 256 sequences at 8k context with the
+ * table's 128 splits), and PA_ERR_HIP when the array's device address
+ * cannot be found.  Nothing is allocated or freed, by this call or by the
+ * library on its behalf.
+ * Sharing: every call on one GPU uses that GPU's one array.  Calls that
+ * overlap on one GPU (other streams, other threads) race and their results
+ * are undefined; calls ordered on one stream are safe.  The array keeps the
+ * last call's contents: what a call needs at zero (the arrival counters of
+ * the fused merge, variant bit 1 clear) it clears itself with a fill kernel
+ * before the decode kernel, and everything else it reads it has written
+ * itself.  The first call on a GPU looks the array's address up (with that
+ * GPU made current for the lookup, then the caller's device restored):
+ * make that first call outside any graph capture. */
+pa_status pa_decode_noalloc(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens, void* out,
+                            float* lse, hipStream_t stream);
+
 /* Prefill / chunked prefill / mixed batch in one launch: sequence s owns
  * query rows [query_start_loc[s], query_start_loc[s+1]); those tokens are
  * the last q_len(s) positions of its context (already written to the pages),

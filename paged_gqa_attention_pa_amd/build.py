@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_decode.hip", "pa_reduce.hip", "pa_prefill.hip", "pa_verify.hip",
            "pa_verify_d64.hip", "pa_verify_d128.hip", "pa_verify_d256.hip", "pa_append.hip",
-           "pa_check.hip",
+           "pa_check.hip", "pa_noalloc.hip",
            "pa_api.cpp"]
 ARCH = "gfx950"
 

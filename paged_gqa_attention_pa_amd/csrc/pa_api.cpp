@@ -220,6 +220,118 @@ pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const voi
       pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, unit_rows, stream));
 }
 
+pa_status check_decode(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                       const int32_t* context_lens, const void* out) {
+  pa_status st = check_attention(problem);
+  if (st != PA_OK) return st;
+  if ((st = check_tiles(tiles)) != PA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  if (problem->max_query_len > 1) return PA_ERR_INVALID_ARG;  // one token per sequence
+  const int G = problem->num_q_heads / problem->num_kv_heads;
+  const int waves = tiles->waves_per_wg;
+  if (short_path(problem, tiles)) return PA_OK;  // the short-run kernel ignores the waves
+  if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
+  if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
+  // the even-work grid merges in the separate kernel only
+  if (even_grid(tiles) && (tiles->variant & pa::kVariantSeparateMerge) == 0)
+    return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// Decode on the decode kernels with the fused last-workgroup merge: the
+// workspace's arrival counters must be zero when the call starts.
+bool uses_arrival_counters(const pa_problem* problem, const pa_tiles* tiles) {
+  return !short_path(problem, tiles) && tiles->num_splits > 1 &&
+         (tiles->variant & pa::kVariantSeparateMerge) == 0;
+}
+
+// pa_decode after its checks: the launches, with the workspace laid out as wl.
+pa_status decode_launch(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                        const int32_t* context_lens, void* out, float* lse, void* workspace,
+                        const Workspace& wl, hipStream_t stream) {
+  pa_status st = PA_OK;
+  const int S = tiles->num_splits;
+  const int G = problem->num_q_heads / problem->num_kv_heads;
+  const int waves = tiles->waves_per_wg;
+  const bool even = even_grid(tiles);
+  if (problem->num_seqs == 0) return PA_OK;
+  if (short_path(problem, tiles))  // G = 32, head dims other than 128, or asked for
+    return short_runs(problem, tiles, q, nullptr, k_pool, v_pool, block_tables, context_lens, out,
+                      lse, static_cast<char*>(workspace), wl, stream);
+
+  const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
+  pa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = static_cast<const uint16_t*>(k_pool);
+  p.v_pool = static_cast<const uint16_t*>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  p.counters = nullptr;
+  p.piece_counts = nullptr;
+  p.query_start_loc = nullptr;
+  if (S > 1) {
+    char* ws = static_cast<char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    p.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+    p.counters = reinterpret_cast<int32_t*>(ws + wl.ctr_off);
+    p.piece_counts = reinterpret_cast<int32_t*>(ws + wl.cnt_off);
+  }
+  p.stride_page = problem->kv_stride_page;
+  p.stride_token = problem->kv_stride_token;
+  p.stride_head = problem->kv_stride_head;
+  p.num_seqs = problem->num_seqs;
+  p.num_q_heads = problem->num_q_heads;
+  p.num_kv_heads = problem->num_kv_heads;
+  p.max_blocks = problem->max_blocks_per_seq;
+  p.num_splits = even ? S + 1 : S;
+  p.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
+  p.max_tiles = ntiles;
+  p.even_min_tiles = p.tiles_per_split;
+  p.scale_log2 = problem->scale * pa::kLog2eHost;
+  p.out_f32 = problem->out_dtype == PA_FP32;
+  p.causal = problem->causal;
+  const bool separate = S > 1 && (tiles->variant & pa::kVariantSeparateMerge) != 0;
+  if (even) {
+    const int nw = pa::decode_even_resident(G, waves, stream);
+    if (nw <= 0) return PA_ERR_HIP;
+    if ((st = from_hip(pa::launch_decode_even(p, G, waves, nw, stream))) != PA_OK) return st;
+  } else if ((st = from_hip(pa::launch_decode(p, G, waves, !separate, stream))) != PA_OK) {
+    return st;
+  }
+  if (separate) {
+    pa::ReduceParams r;
+    r.part_o = p.part_o;
+    r.part_lse = p.part_lse;
+    r.out = out;
+    r.lse = lse;
+    r.rows = problem->num_seqs * problem->num_q_heads;
+    r.num_splits = p.num_splits;
+    r.head_dim = problem->head_dim;
+    r.out_f32 = p.out_f32;
+    r.query_start_loc = nullptr;
+    r.num_q_heads = problem->num_q_heads;
+    r.piece_counts = even ? p.piece_counts : nullptr;
+    r.context_lens = context_lens;
+    r.group = G;
+    r.unit_rows = 0;
+    // even grid: merge per (sequence, kv head) unit, its G rows in one
+    // workgroup, the piece count read once
+    st = from_hip(even ? pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, G,
+                                               stream)
+                       : pa::launch_reduce(r, stream));
+  }
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,97 +412,42 @@ pa_status pa_decode(const pa_problem* problem, const pa_tiles* tiles, const void
                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
                     const int32_t* context_lens, void* out, float* lse, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  pa_status st = check_attention(problem);
+  pa_status st = check_decode(problem, tiles, q, k_pool, v_pool, block_tables, context_lens, out);
   if (st != PA_OK) return st;
-  if ((st = check_tiles(tiles)) != PA_OK) return st;
-  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
-    return PA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
-    return PA_ERR_INVALID_ARG;
-  if (problem->max_query_len > 1) return PA_ERR_INVALID_ARG;  // one token per sequence
-  const int S = tiles->num_splits;
-  const int G = problem->num_q_heads / problem->num_kv_heads;
-  const int waves = tiles->waves_per_wg;
-  if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
-  if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
-  const bool even = even_grid(tiles);
-  // the even-work grid merges in the separate kernel only
-  if (even && (tiles->variant & pa::kVariantSeparateMerge) == 0) return PA_ERR_INVALID_ARG;
   const Workspace wl = workspace_layout(problem, tiles);
   if (wl.dec_total > 0 && (!workspace || workspace_bytes < wl.dec_total ||
                            (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
     return PA_ERR_WORKSPACE;
-  if (problem->num_seqs == 0) return PA_OK;
-  if (short_path(problem, tiles))  // G = 32, head dims other than 128, or asked for
-    return short_runs(problem, tiles, q, nullptr, k_pool, v_pool, block_tables, context_lens, out,
-                      lse, static_cast<char*>(workspace), wl, stream);
+  return decode_launch(problem, tiles, q, k_pool, v_pool, block_tables, context_lens, out, lse,
+                       workspace, wl, stream);
+}
 
-  const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
-  pa::DecodeParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k_pool = static_cast<const uint16_t*>(k_pool);
-  p.v_pool = static_cast<const uint16_t*>(v_pool);
-  p.block_tables = block_tables;
-  p.context_lens = context_lens;
-  p.out = out;
-  p.lse = lse;
-  p.part_o = nullptr;
-  p.part_lse = nullptr;
-  p.counters = nullptr;
-  p.piece_counts = nullptr;
-  p.query_start_loc = nullptr;
-  if (S > 1) {
-    char* ws = static_cast<char*>(workspace);
-    p.part_o = reinterpret_cast<float*>(ws + wl.o_off);
-    p.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
-    p.counters = reinterpret_cast<int32_t*>(ws + wl.ctr_off);
-    p.piece_counts = reinterpret_cast<int32_t*>(ws + wl.cnt_off);
+pa_status pa_decode_noalloc(const pa_problem* problem, const pa_tiles* tiles, const void* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens, void* out,
+                            float* lse, hipStream_t stream) {
+  pa_status st = check_decode(problem, tiles, q, k_pool, v_pool, block_tables, context_lens, out);
+  if (st != PA_OK) return st;
+  const Workspace wl = workspace_layout(problem, tiles);
+  if (wl.dec_total > pa::kScratchBytes) return PA_ERR_WORKSPACE;
+  if (problem->num_seqs == 0) return PA_OK;
+  void* ws = nullptr;
+  if (wl.dec_total > 0) {
+    ws = pa::scratch_address(stream);
+    if (!ws) return PA_ERR_HIP;
+    // The array keeps whatever the last call on this GPU left in it; the
+    // fused merge's arrival counters are the only values a call reads
+    // without writing them first, so they are cleared (a fill kernel, which
+    // a graph capture records like any other launch).
+    if (uses_arrival_counters(problem, tiles)) {
+      const int64_t units = (int64_t)problem->num_seqs * problem->num_kv_heads;
+      if ((st = from_hip(pa::launch_zero_words(static_cast<char*>(ws) + wl.ctr_off, units,
+                                               stream))) != PA_OK)
+        return st;
+    }
   }
-  p.stride_page = problem->kv_stride_page;
-  p.stride_token = problem->kv_stride_token;
-  p.stride_head = problem->kv_stride_head;
-  p.num_seqs = problem->num_seqs;
-  p.num_q_heads = problem->num_q_heads;
-  p.num_kv_heads = problem->num_kv_heads;
-  p.max_blocks = problem->max_blocks_per_seq;
-  p.num_splits = even ? S + 1 : S;
-  p.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
-  p.max_tiles = ntiles;
-  p.even_min_tiles = p.tiles_per_split;
-  p.scale_log2 = problem->scale * pa::kLog2eHost;
-  p.out_f32 = problem->out_dtype == PA_FP32;
-  p.causal = problem->causal;
-  const bool separate = S > 1 && (tiles->variant & pa::kVariantSeparateMerge) != 0;
-  if (even) {
-    const int nw = pa::decode_even_resident(G, waves, stream);
-    if (nw <= 0) return PA_ERR_HIP;
-    if ((st = from_hip(pa::launch_decode_even(p, G, waves, nw, stream))) != PA_OK) return st;
-  } else if ((st = from_hip(pa::launch_decode(p, G, waves, !separate, stream))) != PA_OK) {
-    return st;
-  }
-  if (separate) {
-    pa::ReduceParams r;
-    r.part_o = p.part_o;
-    r.part_lse = p.part_lse;
-    r.out = out;
-    r.lse = lse;
-    r.rows = problem->num_seqs * problem->num_q_heads;
-    r.num_splits = p.num_splits;
-    r.head_dim = problem->head_dim;
-    r.out_f32 = p.out_f32;
-    r.query_start_loc = nullptr;
-    r.num_q_heads = problem->num_q_heads;
-    r.piece_counts = even ? p.piece_counts : nullptr;
-    r.context_lens = context_lens;
-    r.group = G;
-    r.unit_rows = 0;
-    // even grid: merge per (sequence, kv head) unit, its G rows in one
-    // workgroup, the piece count read once
-    st = from_hip(even ? pa::launch_unit_merge(r, problem->num_seqs * problem->num_kv_heads, G,
-                                               stream)
-                       : pa::launch_reduce(r, stream));
-  }
-  return st;
+  return decode_launch(problem, tiles, q, k_pool, v_pool, block_tables, context_lens, out, lse,
+                       ws, wl, stream);
 }
 
 pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const void* q,

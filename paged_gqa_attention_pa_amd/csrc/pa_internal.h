@@ -15,6 +15,8 @@ constexpr int kMaxSplits = 256;        // decode split-KV
 constexpr int kReduceMaxSplits = 4096; // pa_splitkv_reduce
 constexpr int kMaxTileSplits = 8;      // prefill: splits of one query tile's keys
 constexpr float kLog2eHost = 1.4426950408889634f;
+// Bytes of the per-device scratch array behind pa_decode_noalloc.
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
 
 // pa_tiles.variant bits
 constexpr int kVariantPreciseP = 1;      // prefill: P as bf16 high + remainder
@@ -168,6 +170,11 @@ int verify_resident(int group, int rb, bool precise_p, int head_dim, hipStream_t
 hipError_t launch_verify(const DecodeParams& p, int group, int rb, bool precise_p, int head_dim,
                          int nw, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+// pa_decode_noalloc's scratch array: its device address on the device of
+// `stream` (looked up once per device), or null on failure.
+void* scratch_address(hipStream_t stream);
+// Zero `words` 32-bit words at p with a fill kernel on `stream`.
+hipError_t launch_zero_words(void* p, int64_t words, hipStream_t stream);
 hipError_t launch_tile_merge(const TileMergeParams& p, int nx, int head_dim, hipStream_t stream);
 
 }  // namespace pa

@@ -18,8 +18,10 @@ _lib = None
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 PA_BF16, PA_FP32 = 0, 1
 
-EXPORTED = ["pa_select_tiles", "pa_workspace_size", "pa_decode", "pa_prefill",
-            "pa_splitkv_reduce", "pa_cache_append", "pa_check_inputs", "pa_status_string"]
+EXPORTED = ["pa_select_tiles", "pa_workspace_size", "pa_decode", "pa_decode_noalloc",
+            "pa_prefill", "pa_splitkv_reduce", "pa_cache_append", "pa_check_inputs",
+            "pa_status_string"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
 # pa_check_inputs bits
 CHECK_PAGE, CHECK_CONTEXT_BOUND, CHECK_CONTEXT_BLOCKS = 1, 2, 4
 CHECK_QUERY_STARTS, CHECK_QUERY_LEN, CHECK_CONTEXT_SHORT = 8, 16, 32
@@ -68,6 +70,7 @@ def load() -> ctypes.CDLL:
         lib.pa_workspace_size.argtypes = [PP(Problem), PP(Tiles), PP(ctypes.c_size_t)]
         lib.pa_decode.argtypes = [PP(Problem), PP(Tiles), P, P, P, P, P, P, P, P,
                                   ctypes.c_size_t, P]
+        lib.pa_decode_noalloc.argtypes = [PP(Problem), PP(Tiles), P, P, P, P, P, P, P, P]
         lib.pa_prefill.argtypes = [PP(Problem), PP(Tiles), P, P, P, P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
         lib.pa_splitkv_reduce.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -219,6 +222,34 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _check(lib.pa_decode(ctypes.byref(problem), ctypes.byref(tiles), _ptr(q), _ptr(k_pool),
                          _ptr(v_pool), _ptr(block_tables), _ptr(context_lens), _ptr(out),
                          _ptr(lse), _ptr(workspace), wsb, _stream(q.device)), "pa_decode")
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                   max_context_len: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                   tiles: Optional[Tiles] = None,
+                   problem: Optional[Problem] = None) -> torch.Tensor:
+    """pa_decode_noalloc: pa_decode with the library's per-GPU scratch array
+    in place of a workspace.  `out` must be given (this call allocates no
+    device memory; tiles come from pa_select_tiles when None, a host-only
+    lookup)."""
+    lib = load()
+    B = q.shape[0]
+    _check_tensors(q, k_pool, v_pool, block_tables, context_lens, out, lse)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("decode needs one block-table row and one length per query row")
+    if problem is None:
+        problem = make_problem(q, k_pool, block_tables, B, scale, max_context_len, 1,
+                               causal=True, out_dtype=out.dtype)
+    else:
+        _check_problem(problem, q, out, k_pool, block_tables, B)
+    if tiles is None:
+        tiles, _ = select_tiles(problem)
+    _check(lib.pa_decode_noalloc(ctypes.byref(problem), ctypes.byref(tiles), _ptr(q),
+                                 _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                 _ptr(context_lens), _ptr(out), _ptr(lse), _stream(q.device)),
+           "pa_decode_noalloc")
     return out
 
 
