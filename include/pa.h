@@ -79,9 +79,7 @@ typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment          */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128/256,
-                             page size != 16, G not in {1,2,4,8,16,32}, and
-                             at head_dim 256 query runs beyond the short-run
-                             kernel (max_query_len * G > 32)                */
+                             page size != 16, G not in {1,2,4,8,16,32}      */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
   PA_ERR_HIP = 4          /* a HIP launch failed                            */
 } pa_status;
@@ -165,7 +163,7 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
  * counters: it must be zero-filled before its first use, and every call
  * leaves the counters zero again, so it can be reused (and captured) without
  * clearing.  Calls that share one workspace must not run concurrently.
- * tiles->waves_per_wg is 4 or 8 (4 when G = 16).  Pointers to bf16 data must
+ * tiles->waves_per_wg is 4 or 8.  Pointers to bf16 data must
  * be 16-byte aligned.  problem->max_query_len must be 0 or 1.
  * G = 32 (the decode kernels hold at most 16 query heads per KV head) runs
  * on the short-run kernel described at pa_prefill: one token of 32 heads is
@@ -215,13 +213,15 @@ pa_status pa_decode_noalloc(const pa_problem* problem, const pa_tiles* tiles, co
  * other.  Query length 1 rows (decode sequences) may be mixed in, in any
  * order, as one launch ([IBM-PA], unified kernel for mixed batches):
  * sequences with more than one query token are cut into tiles of
- * q_tokens_per_tile tokens x G heads, each walking its allowed keys; when
- * the bounds admit single-token sequences (max_query_len <= 1, or
- * total_query_tokens < num_seqs * max_query_len) and G <= 8, the same launch
+ * q_tokens_per_tile tokens x G heads (a 256-row Q-block, 128 rows at head
+ * dim 256), each walking its allowed keys; when the bounds admit
+ * single-token sequences (max_query_len <= 1, or total_query_tokens <
+ * num_seqs * max_query_len), G <= 8 and head_dim is 128, the same launch
  * also holds split-KV decode workgroups for every (sequence, kv head,
  * split), which return at once for sequences whose query length is not 1.
  * Their partials are merged by a second kernel when tiles->num_splits > 1.
- * With G = 16 or 32 single-token sequences take the tile path.
+ * Otherwise (G = 16 or 32, head dims 64 and 256) single-token sequences
+ * take the tile path.
  * The host picks the kernels from the problem's bounds alone:
  *   - max_query_len <= 1 (G <= 16): the decode kernels, with query_start_loc
  *     mapping the rows (sequences with no query token are skipped);

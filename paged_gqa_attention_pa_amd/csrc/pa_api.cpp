@@ -86,14 +86,13 @@ bool verify_path(const pa_problem* pb) {
   return pb->max_query_len >= 2 && pa::verify_row_blocks(G, pb->max_query_len, pb->head_dim) > 0;
 }
 
-// Head dim 256 is built for decode and short query runs only (the query-tile
-// kernel is built for 64 and 128: its LDS ring of four K and five V tiles
-// would not fit at 256).
-pa_status check_attention(const pa_problem* pb) {
-  pa_status st = check_problem(pb);
-  if (st != PA_OK) return st;
-  if (pb->head_dim == 256 && !verify_path(pb)) return PA_ERR_UNSUPPORTED;
-  return PA_OK;
+pa_status check_attention(const pa_problem* pb) { return check_problem(pb); }
+
+// Query tokens of one query tile: the Q-block (256 rows, 128 at head dim
+// 256) over the G heads of a KV head.
+int query_tile_tokens(const pa_problem* pb) {
+  const int G = pb->num_q_heads / pb->num_kv_heads;
+  return (pb->head_dim == 256 ? 128 : 256) / G;
 }
 
 // Rows of the short-run partials: (token, q head) pairs; a decode-layout
@@ -235,7 +234,6 @@ pa_status check_decode(const pa_problem* problem, const pa_tiles* tiles, const v
   const int waves = tiles->waves_per_wg;
   if (short_path(problem, tiles)) return PA_OK;  // the short-run kernel ignores the waves
   if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
-  if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
   // the even-work grid merges in the separate kernel only
   if (even_grid(tiles) && (tiles->variant & pa::kVariantSeparateMerge) == 0)
     return PA_ERR_INVALID_ARG;
@@ -385,8 +383,8 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     t.tile_splits = 0;
   } else {
     t.kv_tile = 32;
-    t.waves_per_wg = 8;
-    t.q_tokens_per_tile = 256 / G;
+    t.waves_per_wg = problem->head_dim == 256 ? 4 : 8;
+    t.q_tokens_per_tile = query_tile_tokens(problem);
     // single-token sequences of a mixed batch run as split-KV decode work
     t.num_splits = may_hold_decode_rows(problem) ? dc.splits : 1;
     // fp32 outputs ask for more than bf16 weights give: keep P to ~2^-18;
@@ -480,7 +478,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   if (short_path(problem, tiles))
     return short_runs(problem, tiles, q, query_start_loc, k_pool, v_pool, block_tables,
                       context_lens, out, lse, static_cast<char*>(workspace), wl, stream);
-  const int qt = 256 / G;
+  const int qt = query_tile_tokens(problem);
   const float scale_log2 = problem->scale * pa::kLog2eHost;
   const int out_f32 = problem->out_dtype == PA_FP32;
 
@@ -560,8 +558,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
     // are always merged by the separate kernel here
     const int waves = tiles->waves_per_wg;
     if (waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
-    if (G == 16 && waves != 4) return PA_ERR_UNSUPPORTED;
-    if (even) {
+      if (even) {
       const int nw = pa::decode_even_resident(G, waves, stream);
       if (nw <= 0) return PA_ERR_HIP;
       if ((st = from_hip(pa::launch_decode_even(d, G, waves, nw, stream))) != PA_OK) return st;

@@ -28,12 +28,7 @@ hipError_t launch_w(const DecodeParams& p, int group, dim3 grid, hipStream_t str
     case 2: hipLaunchKernelGGL((decode_kernel<2, W, FUSED>), grid, block, 0, stream, p); break;
     case 4: hipLaunchKernelGGL((decode_kernel<4, W, FUSED>), grid, block, 0, stream, p); break;
     case 8: hipLaunchKernelGGL((decode_kernel<8, W, FUSED>), grid, block, 0, stream, p); break;
-    case 16:
-      if constexpr (W == 4) {
-        hipLaunchKernelGGL((decode_kernel<16, 4, FUSED>), grid, block, 0, stream, p);
-        break;
-      }
-      return hipErrorInvalidValue;
+    case 16: hipLaunchKernelGGL((decode_kernel<16, W, FUSED>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -52,9 +47,7 @@ const void* even_kernel_ptr(int group) {
     case 2: return reinterpret_cast<const void*>(&decode_even_kernel<2, W>);
     case 4: return reinterpret_cast<const void*>(&decode_even_kernel<4, W>);
     case 8: return reinterpret_cast<const void*>(&decode_even_kernel<8, W>);
-    case 16:
-      if constexpr (W == 4) return reinterpret_cast<const void*>(&decode_even_kernel<16, 4>);
-      return nullptr;
+    case 16: return reinterpret_cast<const void*>(&decode_even_kernel<16, W>);
     default: return nullptr;
   }
 }

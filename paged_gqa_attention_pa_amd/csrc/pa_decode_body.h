@@ -88,7 +88,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   static_assert(!(FUSED && EVEN), "the even-work grid merges in a separate kernel");
   constexpr int DEPTH = G <= 4 ? 3 : 2;  // tiles per wavefront ring (in flight + computing)
   constexpr int D = kHeadDim;
-  static_assert(G * W <= 64, "LDS budget: W x G x D floats");
+  static_assert(G * W <= 128, "LDS budget: W x G x D floats (64 KiB at G = 16, W = 8)");
   const int tid = threadIdx.x;
   // Query / output row of sequence b: b itself, or its single query token
   // inside a mixed batch (sequences with more query tokens are not decode

@@ -64,6 +64,29 @@ __global__ __launch_bounds__(kThreads, 2) void unified_kernel(PrefillParams pp, 
   }
 }
 
+// Head dim 256: query tiles only (single-token sequences take the tiles
+// too), four wavefronts with the whole register file of their SIMD.
+template <int G, bool PRECISE>
+__global__ __launch_bounds__(64 * prefill_detail::waves_of<256>(), 1) void prefill256_kernel(
+    PrefillParams pp, DecodeParams dp, int nx) {
+  __shared__ __attribute__((aligned(16))) char smem[prefill_smem_bytes<256>()];
+  (void)dp;
+  prefill_body<G, PRECISE, 256>(pp, blockIdx.x, nx, smem);
+}
+
+template <bool PRECISE>
+const void* prefill256_ptr(int group) {
+  switch (group) {
+    case 1: return reinterpret_cast<const void*>(&prefill256_kernel<1, PRECISE>);
+    case 2: return reinterpret_cast<const void*>(&prefill256_kernel<2, PRECISE>);
+    case 4: return reinterpret_cast<const void*>(&prefill256_kernel<4, PRECISE>);
+    case 8: return reinterpret_cast<const void*>(&prefill256_kernel<8, PRECISE>);
+    case 16: return reinterpret_cast<const void*>(&prefill256_kernel<16, PRECISE>);
+    case 32: return reinterpret_cast<const void*>(&prefill256_kernel<32, PRECISE>);
+    default: return nullptr;
+  }
+}
+
 template <bool PRECISE, int D>
 const void* unified_ptr(int group) {
   switch (group) {
@@ -81,6 +104,7 @@ const void* unified_kernel_of(int group, bool precise, int head_dim) {
   if (head_dim == 64) return precise ? unified_ptr<true, 64>(group) : unified_ptr<false, 64>(group);
   if (head_dim == kHeadDim)
     return precise ? unified_ptr<true, kHeadDim>(group) : unified_ptr<false, kHeadDim>(group);
+  if (head_dim == 256) return precise ? prefill256_ptr<true>(group) : prefill256_ptr<false>(group);
   return nullptr;
 }
 
@@ -120,7 +144,8 @@ hipError_t launch_prefill(const PrefillParams& pp, const DecodeParams& dp, int g
   int c = nx;
   void* args[] = {&a, &b, &c};
   const unsigned grid = (unsigned)((int64_t)nx * pp.num_kv_heads * pp.tile_splits + n_dec);
-  return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, 0, stream);
+  const unsigned block = head_dim == 256 ? 64 * prefill_detail::waves_of<256>() : kThreads;
+  return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, stream);
 }
 
 }  // namespace pa

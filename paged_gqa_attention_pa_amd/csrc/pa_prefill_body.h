@@ -38,38 +38,56 @@
 namespace pa {
 namespace prefill_detail {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;            // wavefronts per workgroup at head dims 64 and 128
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;   // Q-block rows per workgroup
 constexpr int kKvTile = 32;          // keys per inner step
+// Head dim 256 holds 128 output accumulators per lane for its 32 rows, so
+// its workgroup is four wavefronts, one per SIMD with the whole register
+// file, and its Q-block 128 rows.
+template <int D>
+constexpr int waves_of() {
+  return D == 256 ? 4 : kWaves;
+}
+template <int D>
+constexpr int rows_of() {
+  return 32 * waves_of<D>();
+}
 // K and V LDS rows (bf16 elements) for head dim D: K rows padded by 8
 // (272 B at D = 128), V rows by 48 (352 B at 128: the four rows of a
-// transposing read group fall on disjoint banks).
+// transposing read group fall on disjoint banks); at 256, V rows are padded
+// by 16 (544 B: rows 8 banks apart, again disjoint over a group's four rows)
+// so that the ring fits in LDS.
 template <int D>
 constexpr int k_stride() {
   return D + 8;
 }
 template <int D>
 constexpr int v_stride() {
-  return D + 48;
+  return D == 256 ? D + 16 : D + 48;
 }
 constexpr int kKBufs = 4;                 // LDS K tile buffers
 constexpr int kVBufs = 5;                 // LDS V tile buffers (V is read one step later)
-constexpr int kPageCache = 2048;          // block-table entries staged in LDS (32k keys)
+// block-table entries staged in LDS: 2048 (32k keys), 1024 (16k keys) at 256
+template <int D>
+constexpr int page_cache() {
+  return D == 256 ? 1024 : 2048;
+}
 constexpr float kLazyThreshold = 8.0f;
 
 // Find (sequence, query tile) of workgroup x: tiles are numbered sequence by
 // sequence, ceil(q_len / qt) per sequence (none for single-token sequences
 // when skip_single: those run as decode workgroups).  Returns false for a
-// surplus x.
+// surplus x.  W: wavefronts of the calling workgroup.
+template <int W = kWaves>
 __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool skip_single,
                           int* seq, int* tile) {
   __shared__ int s_found[2];
-  __shared__ int s_wsum[kWaves];
+  __shared__ int s_wsum[W];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_found[0] = -1;
   int base = 0;
-  for (int c0 = 0; c0 < num_seqs; c0 += 64 * kWaves) {
+  for (int c0 = 0; c0 < num_seqs; c0 += 64 * W) {
     const int s = c0 + tid;
     int cnt = 0;
     if (s < num_seqs) {
@@ -87,7 +105,7 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool 
     __syncthreads();
     int wbase = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       if (w < wave) wbase += s_wsum[w];
       total += s_wsum[w];
     }
@@ -109,21 +127,23 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool 
 template <int D = kHeadDim>
 constexpr int prefill_smem_bytes() {
   return kKBufs * kKvTile * k_stride<D>() * 2 + kVBufs * kKvTile * v_stride<D>() * 2 +
-         kPageCache * 4;
+         page_cache<D>() * 4;
 }
 
-// One workgroup of kThreads threads: query tile / split / KV head number `id`
-// of the 1-D prefill grid (nx tiles x tile_splits x Hkv), head dim D (64 or
-// 128).  smem: prefill_smem_bytes<D>(), 16-byte aligned.
+// One workgroup of 64 * waves_of<D>() threads: query tile / split / KV head
+// number `id` of the 1-D prefill grid (nx tiles x tile_splits x Hkv), head
+// dim D (64, 128 or 256).  smem: prefill_smem_bytes<D>(), 16-byte aligned.
 template <int G, bool PRECISE, int D = kHeadDim>
 __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int nx,
                                              char* smem) {
-  static_assert(D == 64 || D == 128, "query tiles are built for head dims 64 and 128");
+  static_assert(D == 64 || D == 128 || D == 256, "query tiles are built for 64, 128 and 256");
+  constexpr int W = waves_of<D>();
+  constexpr int T = 64 * W;   // threads
   constexpr int kLdsStride = k_stride<D>();
   constexpr int kVStride = v_stride<D>();
   constexpr int KS = D / 16;  // k-steps of the S^T MFMA
   constexpr int MT = D / 32;  // 32-dim M tiles of O^T
-  constexpr int QT = kRows / G;
+  constexpr int QT = rows_of<D>() / G;
   // 1-D grid: id -> (kv head, split, query tile).  Consecutive ids go to
   // different XCDs, so with Hkv = 8 each XCD serves one KV head and its K/V
   // stay in that XCD's L2.  Query tiles run from the last (heaviest under the
@@ -133,7 +153,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   const int split = (id / p.num_kv_heads) % nsplit;
   const int x = nx - 1 - id / (p.num_kv_heads * nsplit);
   int s, qtile;
-  if (!find_tile(p.query_start_loc, p.num_seqs, QT, x, p.decode_rows_apart != 0, &s, &qtile))
+  if (!find_tile<W>(p.query_start_loc, p.num_seqs, QT, x, p.decode_rows_apart != 0, &s, &qtile))
     return;
 
   const int tid = threadIdx.x;
@@ -146,7 +166,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   const int ntok = min(QT, qlen - tok0);
 
   // This lane's row: token r / G, head r % G.
-  const int r = 32 * wave + n;
+  const int r = 32 * wave + n;  // < 32 W
   const int tl = r / G, h = r % G;
   const bool row_valid = tl < ntok;
   const int qi = tok0 + tl;  // index of the token inside the chunk
@@ -186,12 +206,18 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // of key t / 16, dims 8*(t%16) .. +7 (a wavefront moves four whole
   // 256-byte rows of each), so every wavefront does the same staging work.
   // D = 64: a tile is 256 chunks of 16 bytes for K and as many for V, so
-  // wavefronts 0..3 stage K and 4..7 stage V.  Loads are unconditional (a
-  // key past the context reads a valid page and its V row is zeroed when
-  // stored), so no load sits under a branch and the compiler keeps them in
-  // flight across the loop.
+  // wavefronts 0..3 stage K and 4..7 stage V.  D = 256 (256 threads): a tile
+  // is 1024 chunks of each, so thread t stages chunk t % 32 of keys
+  // t / 32 + 8i, i = 0..3 (keys 0..15 of the tile's first page, 16..31 of
+  // its second).  Loads are unconditional (a key past the context reads a
+  // valid page and its V row is zeroed when stored), so no load sits under a
+  // branch and the compiler keeps them in flight across the loop.
   constexpr int CH = D / 8;  // 16-byte chunks per row
-  constexpr bool kSplitKV = 2 * kKvTile * CH <= kThreads;
+  constexpr bool kSplitKV = 2 * kKvTile * CH <= T;
+  constexpr int NC = kSplitKV ? 1 : kKvTile * CH / T;  // chunks of K (and of V) per thread
+  constexpr int KSTEP = T / CH;                          // key step between a thread's chunks
+  static_assert(kSplitKV || NC * T == kKvTile * CH, "whole chunks per thread");
+  static_assert(NC == 1 || (KSTEP * 2 == kPage && NC == 4), "multi-chunk staging: D = 256");
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks;
   const int ti = kSplitKV ? tid % (kKvTile * CH) : tid;
   const bool stage_v = kSplitKV && tid >= kKvTile * CH;  // wavefront-uniform
@@ -199,47 +225,75 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   const int64_t loff = (int64_t)g * p.stride_head + (int64_t)(lkey % kPage) * p.stride_token + 8 * ldc;
   const char* kth = reinterpret_cast<const char*>(p.k_pool + loff);
   const char* vth = reinterpret_cast<const char*>(p.v_pool + loff);
+  // multi-chunk staging: the odd chunks sit KSTEP slots further into a page
+  const uint32_t odd_bytes = (uint32_t)(KSTEP * p.stride_token * 2);
   const uint32_t page_bytes = (uint32_t)(p.stride_page * 2);  // < 2^32 (checked on the host)
   // Page ids of the current window of key tiles, staged in LDS, keep the
   // block-table lookup off each tile's load path.  Entries past the
   // context hold page 0 (never used: those keys are masked and zeroed).
   int* pg_lds = reinterpret_cast<int*>(smem + kKBufs * kKvTile * kLdsStride * 2 +
                                        kVBufs * kKvTile * kVStride * 2);
-  constexpr int kWinTiles = kPageCache * kPage / kKvTile;
+  constexpr int kWinTiles = page_cache<D>() * kPage / kKvTile;
   const int nblk = (L + kPage - 1) / kPage;  // valid block-table entries
   int win0 = 0;                              // first key tile of the window
-  // tile t of the window -> r[0] = K, r[1] = V (split: r[0] = this thread's
-  // K or V chunk)
-  auto load_tile = [&](int t, uint4 (&r)[2]) {
-    const uint64_t off =
-        (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + lkey / kPage] * page_bytes;
+  // tile t of the window -> r[i] = K chunk i, r[NC + i] = V chunk i (split:
+  // r[0] = this thread's K or V chunk)
+  constexpr int NR = kSplitKV ? 1 : 2 * NC;
+  auto load_tile = [&](int t, uint4 (&r)[NR]) {
     if constexpr (kSplitKV) {
+      const uint64_t off =
+          (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + lkey / kPage] * page_bytes;
       r[0] = *reinterpret_cast<const uint4*>((stage_v ? vth : kth) + off);
-    } else {
+    } else if constexpr (NC == 1) {
+      const uint64_t off =
+          (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + lkey / kPage] * page_bytes;
       r[0] = *reinterpret_cast<const uint4*>(kth + off);
       r[1] = *reinterpret_cast<const uint4*>(vth + off);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const uint64_t off =
+            (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + i / 2] * page_bytes +
+            ((i & 1) ? odd_bytes : 0u);
+        r[i] = *reinterpret_cast<const uint4*>(kth + off);
+        r[NC + i] = *reinterpret_cast<const uint4*>(vth + off);
+      }
     }
   };
-  auto store_tile = [&](int t, int kbuf, int vbuf, const uint4 (&r)[2]) {
+  auto store_tile = [&](int t, int kbuf, int vbuf, const uint4 (&r)[NR]) {
     // V rows past the context are zeroed: stale data (even NaN) must not
     // reach O through a zero weight
     const bool tail = (win0 + t + 1) * kKvTile > L;  // uniform
-    const bool dead = tail && (win0 + t) * kKvTile + lkey >= L;
     // element-wise copies: a whole-struct copy becomes a memcpy that can
     // keep the staging registers in memory
-    const uint32_t keep = dead ? 0u : ~0u;
-    if constexpr (kSplitKV) {
-      if (stage_v)
-        *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
-            make_uint4(r[0].x & keep, r[0].y & keep, r[0].z & keep, r[0].w & keep);
-      else
+    if constexpr (kSplitKV || NC == 1) {
+      const bool dead = tail && (win0 + t) * kKvTile + lkey >= L;
+      const uint32_t keep = dead ? 0u : ~0u;
+      if constexpr (kSplitKV) {
+        if (stage_v)
+          *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
+              make_uint4(r[0].x & keep, r[0].y & keep, r[0].z & keep, r[0].w & keep);
+        else
+          *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) =
+              make_uint4(r[0].x, r[0].y, r[0].z, r[0].w);
+      } else {
         *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) =
             make_uint4(r[0].x, r[0].y, r[0].z, r[0].w);
+        *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
+            make_uint4(r[1].x & keep, r[1].y & keep, r[1].z & keep, r[1].w & keep);
+      }
     } else {
-      *reinterpret_cast<uint4*>(&k_lds[kbuf][lkey * kLdsStride + 8 * ldc]) =
-          make_uint4(r[0].x, r[0].y, r[0].z, r[0].w);
-      *reinterpret_cast<uint4*>(&v_lds[vbuf][lkey * kVStride + 8 * ldc]) =
-          make_uint4(r[1].x & keep, r[1].y & keep, r[1].z & keep, r[1].w & keep);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int key = lkey + KSTEP * i;
+        const bool dead = tail && (win0 + t) * kKvTile + key >= L;
+        const uint32_t keep = dead ? 0u : ~0u;
+        *reinterpret_cast<uint4*>(&k_lds[kbuf][key * kLdsStride + 8 * ldc]) =
+            make_uint4(r[i].x, r[i].y, r[i].z, r[i].w);
+        *reinterpret_cast<uint4*>(&v_lds[vbuf][key * kVStride + 8 * ldc]) =
+            make_uint4(r[NC + i].x & keep, r[NC + i].y & keep, r[NC + i].z & keep,
+                       r[NC + i].w & keep);
+      }
     }
   };
   // Transposing V reads: lane (group gq = lane / 16, r = lane % 16) points
@@ -395,19 +449,19 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // wavefront-uniform, and visibly so to the compiler (readfirstlane), so
   // the extra barriers below sit behind scalar branches: a wavefront that
   // does not take them never executes them
-  const bool lag = __builtin_amdgcn_readfirstlane(wave) >= kWaves / 2;
+  const bool lag = __builtin_amdgcn_readfirstlane(wave) >= W / 2;
   for (int wbeg = 0; wbeg < nkv; wbeg += kWinTiles) {
     const int nw = min(kWinTiles, nkv - wbeg);
     win0 = j0 + wbeg;
     {
       const int b0 = win0 * (kKvTile / kPage);
       const int nb = nw * (kKvTile / kPage);
-      for (int i = tid; i < nb; i += kThreads) pg_lds[i] = (b0 + i < nblk) ? bt[b0 + i] : 0;
+      for (int i = tid; i < nb; i += T) pg_lds[i] = (b0 + i < nblk) ? bt[b0 + i] : 0;
       __syncthreads();
     }
     // the first three tiles' loads are all issued before any is stored, so
     // the window start waits on memory once rather than three times
-    uint4 rg[2], r1[2], r2[2];
+    uint4 rg[NR], r1[NR], r2[NR];
     load_tile(0, rg);
     load_tile(min(1, nw - 1), r1);
     load_tile(min(2, nw - 1), r2);

@@ -314,6 +314,9 @@ __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(Ti
                                                                              int nx) {
   using prefill_detail::find_tile;
   constexpr int DPL = D / 32;  // dims per lane: 32 lanes cover a row
+  // rows in flight per wavefront step (two per row pair of half-wavefronts);
+  // fewer at head dim 256, whose rows are twice as many registers
+  constexpr int RPI = DPL == 8 ? 2 : kMergeRowsPerIter;
   const int g = blockIdx.x % p.num_kv_heads;
   const int x = nx - 1 - blockIdx.x / p.num_kv_heads;
   int s, qtile;
@@ -330,27 +333,32 @@ __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(Ti
   const int rows_per_wave = (nrows + prefill_detail::kWaves - 1) / prefill_detail::kWaves;
   const int r_begin = wave * rows_per_wave;
   const int r_end = min(nrows, r_begin + rows_per_wave);
-  for (int r0 = r_begin; r0 < r_end; r0 += kMergeRowsPerIter) {
-    int64_t orow[kMergeRowsPerIter / 2];
-    bool valid[kMergeRowsPerIter / 2];
-    float M[kMergeRowsPerIter / 2];
+  for (int r0 = r_begin; r0 < r_end; r0 += RPI) {
+    int64_t orow[RPI / 2];
+    bool valid[RPI / 2];
+    float M[RPI / 2];
 #pragma unroll
-    for (int u = 0; u < kMergeRowsPerIter / 2; ++u) {
+    for (int u = 0; u < RPI / 2; ++u) {
       const int r = r0 + 2 * u + sub;
       valid[u] = r < r_end;
       const int rr = valid[u] ? r : r_begin;
       orow[u] = (int64_t)(q0 + tok0 + rr / G) * p.num_q_heads + g * G + rr % G;
       M[u] = kNegInf;
     }
-    float lse_v[kMergeRowsPerIter / 2][S];
-    float v[kMergeRowsPerIter / 2][S][DPL];
+    float lse_v[RPI / 2][S];
+    float v[RPI / 2][S][DPL];
 #pragma unroll
-    for (int u = 0; u < kMergeRowsPerIter / 2; ++u)
+    for (int u = 0; u < RPI / 2; ++u)
 #pragma unroll
       for (int k = 0; k < S; ++k) {
         lse_v[u][k] = p.tpart_lse[orow[u] * S + k];
         const float* src = p.tpart_o + (orow[u] * S + k) * D + DPL * dl;
-        if constexpr (DPL == 4) {
+        if constexpr (DPL == 8) {
+          const float4 t0 = *reinterpret_cast<const float4*>(src);
+          const float4 t1 = *reinterpret_cast<const float4*>(src + 4);
+          v[u][k][0] = t0.x; v[u][k][1] = t0.y; v[u][k][2] = t0.z; v[u][k][3] = t0.w;
+          v[u][k][4] = t1.x; v[u][k][5] = t1.y; v[u][k][6] = t1.z; v[u][k][7] = t1.w;
+        } else if constexpr (DPL == 4) {
           const float4 t = *reinterpret_cast<const float4*>(src);
           v[u][k][0] = t.x; v[u][k][1] = t.y; v[u][k][2] = t.z; v[u][k][3] = t.w;
         } else {
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(Ti
         M[u] = fmaxf(M[u], lse_v[u][k]);
       }
 #pragma unroll
-    for (int u = 0; u < kMergeRowsPerIter / 2; ++u) {
+    for (int u = 0; u < RPI / 2; ++u) {
       float acc[DPL];
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
@@ -381,7 +389,17 @@ __global__ __launch_bounds__(prefill_detail::kThreads) void tile_merge_kernel(Ti
       for (int e = 0; e < DPL; ++e) acc[e] *= inv;
       if (!valid[u]) continue;
       const int64_t off = orow[u] * D + DPL * dl;
-      if constexpr (DPL == 4) {
+      if constexpr (DPL == 8) {
+        if (p.out_f32) {
+          float* o = reinterpret_cast<float*>(p.out) + off;
+          *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        } else {
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + off) =
+              make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        }
+      } else if constexpr (DPL == 4) {
         if (p.out_f32)
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) =
               make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -424,6 +442,7 @@ hipError_t launch_tile_merge(const TileMergeParams& p, int nx, int head_dim, hip
   if (nx <= 0) return hipSuccess;
   if (head_dim == 64) return launch_tile_merge_d<64>(p, nx, stream);
   if (head_dim == kHeadDim) return launch_tile_merge_d<kHeadDim>(p, nx, stream);
+  if (head_dim == 256) return launch_tile_merge_d<256>(p, nx, stream);
   return hipErrorInvalidValue;
 }
 

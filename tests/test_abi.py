@@ -107,24 +107,27 @@ def test_group_sizes_built(lib):
 
 
 def test_head_dims_built(lib):
-    """Head dims 64 and 256 are built for decode and short query runs (the
-    short-run kernel); longer runs need the query tiles, built for 64 and
-    128."""
+    """Head dims 64, 128 and 256 are built for decode, short query runs and
+    query tiles; the query tile is 256 rows (256 / G tokens, 8 wavefronts),
+    128 rows at head dim 256 (4 wavefronts)."""
     for d in (64, 128, 256):
         kw = dict(head_dim=d, kv_stride_page=16 * 8 * d, kv_stride_token=8 * d, kv_stride_head=d)
         st, t, ws = _select(lib, _problem(**kw))  # decode
         assert st == pa.PA_OK, d
         st, t, ws = _select(lib, _problem(max_query_len=4, total_query_tokens=16, **kw))
         assert st == pa.PA_OK, d
-        st, _, _ = _select(lib, _problem(max_query_len=64, total_query_tokens=256, **kw))
-        assert st == (pa.PA_ERR_UNSUPPORTED if d == 256 else pa.PA_OK), d
-    # 16 rows x 256 dims per row block: at most two row blocks
+        st, t, _ = _select(lib, _problem(max_query_len=64, total_query_tokens=256, **kw))
+        assert st == pa.PA_OK, d
+        assert t.q_tokens_per_tile == (32 if d == 256 else 64), d
+        assert t.waves_per_wg == (4 if d == 256 else 8), d
+    # 16 rows x 256 dims per row block: at most two row blocks, longer runs
+    # take the query tiles
     kw = dict(head_dim=256, kv_stride_page=16 * 8 * 256, kv_stride_token=8 * 256,
               kv_stride_head=256)
-    st, _, _ = _select(lib, _problem(max_query_len=8, total_query_tokens=32, **kw))
-    assert st == pa.PA_OK
-    st, _, _ = _select(lib, _problem(max_query_len=9, total_query_tokens=36, **kw))
-    assert st == pa.PA_ERR_UNSUPPORTED
+    st, t, _ = _select(lib, _problem(max_query_len=8, total_query_tokens=32, **kw))
+    assert st == pa.PA_OK and t.kv_tile == 16
+    st, t, _ = _select(lib, _problem(max_query_len=9, total_query_tokens=36, **kw))
+    assert st == pa.PA_OK and t.kv_tile == 32 and t.q_tokens_per_tile == 32
 
 
 def test_select_tiles_short_runs(lib):

@@ -119,10 +119,81 @@ def test_prefill_head_dim_64_tile_splits(dev, ts):
         compare(b, out, lse, rows=rows, label=f"prefill D=64 ts={ts} {dt}")
 
 
-def test_long_runs_unsupported_d256(dev):
-    spec = workloads.small_spec("long_d256", seed=970, contexts=[300], queries=[100],
-                                head_dim=256, decode_layout=False)
+PREFILL_D256 = [
+    # (name, contexts, query lens, causal, hq, hkv)
+    ("chunks", [300, 77, 1000, 33], [140, 77, 31, 33], True, 32, 8),
+    ("tiles", [32, 64, 65, 200], [32, 64, 65, 129], True, 32, 8),
+    ("noncausal", [300, 50], [100, 7], False, 32, 8),
+    # single-token sequences take the query tiles at head dim 256
+    ("decode_rows", [900, 40, 260, 513], [1, 1, 100, 200], True, 32, 8),
+    ("g1", [200, 90], [70, 90], True, 8, 8),
+    ("g2", [200, 90], [70, 90], True, 16, 8),
+    ("g8", [200, 90], [70, 90], True, 32, 4),
+    ("g16", [200, 90], [70, 90], True, 16, 1),
+    ("g32", [300, 77], [40, 9], True, 32, 1),
+    # more than 1024 pages: the page-id window (16k keys at 256) is restaged
+    ("long_context", [20000, 300], [32, 20], True, 32, 8),
+]
+
+
+@pytest.mark.parametrize("name,ctx,ql,causal,hq,hkv", PREFILL_D256,
+                         ids=[c[0] for c in PREFILL_D256])
+@pytest.mark.parametrize("out_dtype,with_lse", [(torch.bfloat16, True), (torch.float32, True),
+                                                (torch.bfloat16, False)],
+                         ids=["bf16", "f32", "bf16_nolse"])
+def test_prefill_head_dim_256(dev, name, ctx, ql, causal, hq, hkv, out_dtype, with_lse):
+    """Query tiles at head dim 256: a 128-row Q-block on four wavefronts,
+    each thread staging four 16-byte chunks of K and of V per key tile."""
+    log(f"[prefill D=256 {name} {out_dtype} lse={with_lse}]")
+    spec = workloads.small_spec(f"pf256_{name}", seed=1980 + sum(ql) + hq, contexts=ctx,
+                                queries=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=256,
+                                causal=causal, decode_layout=False)
     b = workloads.generate(spec, dev)
-    with pytest.raises(pa.PAError) as e:
-        run_prefill(b, torch.bfloat16)
-    assert e.value.status == pa.PA_ERR_UNSUPPORTED
+    T = sum(ql) * spec.num_q_heads
+    rows = None
+    if T > 8192:
+        rng = np.random.default_rng(5)
+        rows = np.unique(np.concatenate([rng.choice(T, 4096, replace=False), [0, T - 1]]))
+    out, lse = run_prefill(b, out_dtype, with_lse=with_lse)
+    compare(b, out, lse, rows=rows, label=f"prefill D=256 {name} lse={with_lse}")
+
+
+@pytest.mark.parametrize("ts", [2, 5])
+def test_prefill_head_dim_256_tile_splits(dev, ts):
+    """Split query tiles at head dim 256, merged over a NaN-filled workspace."""
+    log(f"[prefill D=256 tile splits {ts}]")
+    spec = workloads.small_spec("pf256_ts", seed=1990 + ts, contexts=[2100, 1500],
+                                queries=[300, 200], head_dim=256, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    rng = np.random.default_rng(ts)
+    T = 500 * spec.num_q_heads
+    rows = np.unique(np.concatenate([rng.choice(T, 4096, replace=False), [0, T - 1]]))
+    for dt in (torch.bfloat16, torch.float32):
+        out, lse = run_prefill(b, dt, tile_splits=ts, stale_workspace=True)
+        compare(b, out, lse, rows=rows, label=f"prefill D=256 ts={ts} {dt}")
+
+
+def test_prefill_head_dim_256_dominant_logit_bitexact(dev):
+    """Indexing at head dim 256: a dominant logit selects V[t*] exactly."""
+    log("[prefill D=256 dominant logit]")
+    L, q = 300, 40
+    tstars = [0, 31, 32, 200, 259]
+    spec = workloads.small_spec("dom256", seed=1931, contexts=[L] * len(tstars),
+                                queries=[q] * len(tstars), head_dim=256, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    P = spec.page_size
+    b.q.zero_()
+    b.q[:, :, 0] = 64.0
+    for s, t in enumerate(tstars):
+        for j in range(-(-L // P)):
+            b.k_pool[int(b.block_tables[s, j]), :, :, 0] = 0.0
+        b.k_pool[int(b.block_tables[s, t // P]), t % P, :, 0] = 64.0
+    for dt in (torch.bfloat16, torch.float32):
+        out, _ = run_prefill(b, dt, with_lse=False)
+        for s, t in enumerate(tstars):
+            want = b.v_pool[int(b.block_tables[s, t // P]), t % P].repeat_interleave(4, dim=0)
+            got = out[s * q:(s + 1) * q]
+            want = want.to(dt).expand_as(got)
+            ok = (torch.equal(got.view(torch.int16), want.view(torch.int16))
+                  if dt == torch.bfloat16 else torch.equal(got, want))
+            assert ok, f"seq {s} t*={t} {dt}"

@@ -155,8 +155,6 @@ MERGE_VARIANT = {"fused": 0, "separate": 2, "even": 6}
 @pytest.mark.parametrize("merge", ["fused", "separate", "even"])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_decode_small(dev, name, ctx, hq, hkv, splits, waves, merge, out_dtype):
-    if hq // hkv == 16 and waves == 8:
-        pytest.skip("G = 16 is built with 4 waves per workgroup only")
     log(f"[decode {name} splits={splits} waves={waves} {merge} {out_dtype}]")
     spec = workloads.small_spec(f"dec_{name}", seed=100 + len(ctx) + hq, contexts=ctx,
                                 queries=[1] * len(ctx), num_q_heads=hq, num_kv_heads=hkv)
