@@ -23,13 +23,14 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _default = None
 
 
-def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle with gcc (plain C, -O2, pthreads)."""
+def build(force: bool = False, src: str = _SRC, out: str = _LIB, flags=("-O2",)) -> str:
+    """Compile the oracle with gcc (plain C, -O2, pthreads); `flags` replaces
+    the optimisation flags (e.g. a sanitizer build)."""
     if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
         tmp = out + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L",
-                               "-Wall", "-shared", "-fPIC", "-pthread",
-                               src, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc"] + list(flags) + ["-std=c99", "-D_POSIX_C_SOURCE=200809L",
+                                                       "-Wall", "-shared", "-fPIC", "-pthread",
+                                                       src, "-o", tmp, "-lm"])
         os.replace(tmp, out)
     return out
 

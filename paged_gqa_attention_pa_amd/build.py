@@ -36,8 +36,16 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC",
 NOISE = "packed-fp32-ops"  # the host pass warns that it does not know the feature
 
 
-def compile_command(src: str, obj: str):
-    return ([hipcc(), f"--offload-arch={ARCH}"] + FLAGS +
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the C-ABI
+# argument checks (pa_api.cpp), device code untouched; the build loads only
+# with clang's ASan runtime preloaded (a test-only build).
+HOST_SANITIZE = ["-O1", "-g", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def compile_command(src: str, obj: str, extra=()):
+    return ([hipcc(), f"--offload-arch={ARCH}"] + FLAGS + list(extra) +
             ["-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj])
 
 
@@ -51,13 +59,15 @@ def _run(cmd):
     return res.returncode, msg
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, sanitize_host_api: bool = False) -> str:
     """Compile every source (in parallel, one object each) and link libpa.so
-    (always recompiles)."""
+    (always recompiles); sanitize_host_api builds pa_api.cpp with the host
+    sanitizers (for tests; such a build needs clang's ASan runtime preloaded)."""
     tmpdir = tempfile.mkdtemp(prefix="pa_build_")
     try:
         objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        cmds = [compile_command(s, o) for s, o in zip(SOURCES, objs)]
+        cmds = [compile_command(s, o, HOST_SANITIZE if sanitize_host_api and s == "pa_api.cpp"
+                                else ()) for s, o in zip(SOURCES, objs)]
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
@@ -69,16 +79,16 @@ def build(verbose: bool = False) -> str:
                 raise RuntimeError(f"hipcc failed on {src}:\n" + msg)
             if verbose and msg.strip():
                 print(msg)
-        tmp = LIB + ".tmp%d" % os.getpid()
+        tmp = out + ".tmp%d" % os.getpid()
         rc, msg = _run(link_command(objs, tmp))
         if rc != 0:
             if os.path.exists(tmp):
                 os.remove(tmp)
             raise RuntimeError("link failed:\n" + msg)
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

@@ -21,6 +21,20 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 bool group_built(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32; }
 
+// The 32 bits a caller put in a pa_dtype field or argument.  In C++ reading
+// an enum object whose value is none of its enumerators is undefined, so the
+// value is copied out as an integer before it is checked.
+int32_t raw_dtype(const pa_dtype& d) {
+  static_assert(sizeof(pa_dtype) == sizeof(int32_t), "pa_dtype is a 32-bit C enum");
+  int32_t v;
+  memcpy(&v, &d, sizeof v);
+  return v;
+}
+bool dtype_valid(const pa_dtype& d) {
+  const int32_t v = raw_dtype(d);
+  return v == PA_BF16 || v == PA_FP32;
+}
+
 // Checks shared by every call; returns PA_OK or the first failure.
 pa_status check_problem(const pa_problem* pb) {
   if (!pb) return PA_ERR_INVALID_ARG;
@@ -33,7 +47,7 @@ pa_status check_problem(const pa_problem* pb) {
   if (pb->kv_stride_page <= 0 || pb->kv_stride_token <= 0 || pb->kv_stride_head <= 0 ||
       pb->kv_stride_page % 8 || pb->kv_stride_token % 8 || pb->kv_stride_head % 8)
     return PA_ERR_INVALID_ARG;
-  if (pb->out_dtype != PA_BF16 && pb->out_dtype != PA_FP32) return PA_ERR_INVALID_ARG;
+  if (!dtype_valid(pb->out_dtype)) return PA_ERR_INVALID_ARG;
   if (pb->causal != 0 && pb->causal != 1) return PA_ERR_INVALID_ARG;
   if (!(pb->scale > 0.f) || pb->scale == __builtin_inff()) return PA_ERR_INVALID_ARG;
   if ((int64_t)pb->max_context_len > (int64_t)pb->max_blocks_per_seq * pb->page_size)
@@ -377,7 +391,8 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     t.waves_per_wg = 4;
     t.q_tokens_per_tile = problem->max_query_len > 1 ? problem->max_query_len : 1;
     t.num_splits = pa::table_short_splits(problem->num_seqs, problem->num_kv_heads,
-                                          problem->max_context_len, dc.splits);
+                                          problem->max_context_len, problem->head_dim, G,
+                                          dc.splits);
     t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
                 pa::kVariantSeparateMerge | pa::kVariantEvenWork;
     t.tile_splits = 0;
@@ -400,7 +415,7 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
                         ? 1
                         : pa::table_prefill_splits(problem->total_query_tokens,
                                                    t.q_tokens_per_tile, problem->num_kv_heads,
-                                                   problem->max_context_len);
+                                                   problem->max_context_len, problem->head_dim);
   }
   *out = t;
   return pa_workspace_size(problem, &t, workspace_bytes);
@@ -699,7 +714,7 @@ pa_status pa_splitkv_reduce(const float* partial_o, const float* partial_lse, in
   if (rows < 0 || num_splits < 1 || num_splits > pa::kReduceMaxSplits || head_dim <= 0 ||
       head_dim % 4 != 0 || head_dim > 1024)
     return PA_ERR_INVALID_ARG;
-  if (out_dtype != PA_BF16 && out_dtype != PA_FP32) return PA_ERR_INVALID_ARG;
+  if (!dtype_valid(out_dtype)) return PA_ERR_INVALID_ARG;
   if (rows == 0) return PA_OK;
   if (!partial_o || !partial_lse || !out) return PA_ERR_INVALID_ARG;
   if (!aligned16(partial_o) || !aligned16(out)) return PA_ERR_INVALID_ARG;

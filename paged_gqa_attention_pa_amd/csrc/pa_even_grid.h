@@ -2,6 +2,7 @@
 #pragma once
 
 #include "pa_decode_body.h"
+#include "pa_even_plan.h"
 #include "pa_verify_body.h"
 
 namespace pa {
@@ -54,8 +55,7 @@ __device__ void decode_even_body(const DecodeParams& p, int w, int nw, float* sm
   for (int i = 0; i < W; ++i) per_head += s_part[i];
   const long long N = per_head * Hkv;
   if (N == 0) return;
-  const long long wt_fill = (N + nw - 1) / nw;
-  const long long Wt = wt_fill > p.even_min_tiles ? wt_fill : p.even_min_tiles;
+  const long long Wt = even_plan::tiles_per_workgroup(N, nw, p.even_min_tiles);
   const long long R0 = (long long)w * Wt;
   if (R0 >= N) return;
   const long long R1 = R0 + Wt < N ? R0 + Wt : N;
@@ -90,36 +90,26 @@ __device__ void decode_even_body(const DecodeParams& p, int w, int nw, float* sm
     __syncthreads();
     if (s_seq >= 0) break;
   }
-  int b = s_seq;
-  long long P = s_start;
-  int nb = seq_tiles(b);
+  even_plan::Cursor cur{R0, s_start, s_seq, seq_tiles(s_seq)};
   const int S = p.num_splits;  // partial slots per row
-  long long pos = R0;
   while (true) {
-    const long long rel = pos - P * Hkv;
-    const int g = (int)(rel / nb);
-    const int t0 = (int)(rel % nb);
-    const long long take = (long long)(nb - t0) < R1 - pos ? (long long)(nb - t0) : R1 - pos;
-    const int t1 = t0 + (int)take;
-    const long long u0 = P * Hkv + (long long)g * nb;  // first tile of this unit
-    const int w_first = (int)(u0 / Wt);
-    const int w_last = (int)((u0 + nb - 1) / Wt);
-    const int pieces = w_last - w_first + 1;
-    const EvenPiece piece{t0, t1, w - w_first, S, pieces == 1};
+    const even_plan::Piece pc = even_plan::piece_at(cur, R1, Wt, Hkv, w);
+    const int b = cur.b;
+    const EvenPiece piece{pc.t0, pc.t1, pc.slot, S, pc.direct};
     if constexpr (RB == 0)
-      decode_body<G, W, false, true>(p, 0, g, b, sm_buf, piece);
+      decode_body<G, W, false, true>(p, 0, pc.g, b, sm_buf, piece);
     else
-      verify_detail::verify_body<G, RB, W, PRECISE, D>(p, g, b, sm_buf, piece);
-    if (tid == 0 && w == w_last) p.piece_counts[(int64_t)b * Hkv + g] = pieces;
+      verify_detail::verify_body<G, RB, W, PRECISE, D>(p, pc.g, b, sm_buf, piece);
+    if (tid == 0 && pc.last) p.piece_counts[(int64_t)b * Hkv + pc.g] = pc.pieces;
     __syncthreads();  // the next piece reuses the LDS merge buffers
-    pos += take;
-    if (pos >= R1) break;
-    if (g == Hkv - 1 && t1 == nb) {  // next sequence with tiles
-      P += nb;
+    cur.pos += pc.t1 - pc.t0;
+    if (cur.pos >= R1) break;
+    if (even_plan::ends_sequence(pc, cur.nb, Hkv)) {  // next sequence with tiles
+      cur.P += cur.nb;
       do {
-        ++b;
-        nb = seq_tiles(b);
-      } while (nb == 0);
+        ++cur.b;
+        cur.nb = seq_tiles(cur.b);
+      } while (cur.nb == 0);
     }
   }
 }

@@ -32,7 +32,8 @@ inline int table_decode_waves(int num_seqs, int num_kv_heads, int max_context_le
   (void)num_seqs;
   (void)num_kv_heads;
   (void)max_context_len;
-  return group >= 16 ? 4 : 4;
+  (void)group;
+  return 4;
 }
 
 // Decode variant bits (pa_tiles.variant).  Merging the splits in a second
@@ -88,8 +89,17 @@ struct DecodeChoice {
   int splits, waves, variant;
 };
 
-// Decode launch shape: the swept entry for (units, context-bound) bucket when
-// there is one, else the fallback rules.
+// Index of the last entry <= v of an ascending list (0 below the first).
+template <int N>
+inline int index_floor(const int (&vals)[N], int v) {
+  int i = 0;
+  while (i + 1 < N && vals[i + 1] <= v) ++i;
+  return i;
+}
+
+// Decode launch shape: the swept entry for the (G, units, context-bound)
+// bucket when there is one (G rounded down to a swept group), else the
+// fallback rules.
 inline DecodeChoice table_decode(int num_seqs, int num_kv_heads, int max_context_len,
                                  int group) {
   DecodeChoice c{table_decode_splits(num_seqs, num_kv_heads, max_context_len),
@@ -100,12 +110,12 @@ inline DecodeChoice table_decode(int num_seqs, int num_kv_heads, int max_context
                      ? -1
                      : bucket_floor(gen::kUnitBuckets, units);
   const int ci = bucket_of(gen::kCtxBuckets, max_context_len);
-  if (ui >= 0 && ci >= 0 && gen::kDecode[ui][ci][0] > 0) {
-    c.splits = gen::kDecode[ui][ci][0];
-    c.waves = gen::kDecode[ui][ci][1];
-    c.variant = gen::kDecode[ui][ci][2];
+  const int gi = index_floor(gen::kDecodeGroups, group);
+  if (ui >= 0 && ci >= 0 && gen::kDecode[gi][ui][ci][0] > 0) {
+    c.splits = gen::kDecode[gi][ui][ci][0];
+    c.waves = gen::kDecode[gi][ui][ci][1];
+    c.variant = gen::kDecode[gi][ui][ci][2];
   }
-  if (group >= 16) c.waves = 4;  // the only G = 16 build
   if (c.splits <= 1) {
     c.splits = 1;
     c.variant = 2;
@@ -114,28 +124,38 @@ inline DecodeChoice table_decode(int num_seqs, int num_kv_heads, int max_context
 }
 
 // Short query runs (one Q-block per (sequence, kv head) unit): the swept split
-// bound for the (units, context-bound) bucket when there is one, else the
-// decode choice, whose grid it shares.
-inline int table_short_splits(int num_seqs, int num_kv_heads, int max_context_len,
-                              int decode_splits) {
+// bound for the (head dim, G >= 16) key and (units, context-bound) bucket
+// when there is one, else the decode choice, whose grid it shares.
+inline int table_short_splits(int num_seqs, int num_kv_heads, int max_context_len, int head_dim,
+                              int group, int decode_splits) {
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   constexpr int kLast = sizeof(gen::kShortUnitBuckets) / sizeof(int) - 1;
   const int ui = units > 2 * gen::kShortUnitBuckets[kLast]
                      ? -1
                      : bucket_floor(gen::kShortUnitBuckets, units);
   const int ci = bucket_of(gen::kShortCtxBuckets, max_context_len);
-  if (ui >= 0 && ci >= 0 && gen::kShortSplits[ui][ci] > 0) return gen::kShortSplits[ui][ci];
+  int ki = -1;
+  constexpr int kKeys = sizeof(gen::kShortKeys) / sizeof(gen::kShortKeys[0]);
+  for (int k = 0; k < kKeys; ++k)
+    if (gen::kShortKeys[k][0] == head_dim && gen::kShortKeys[k][1] == (group >= 16 ? 1 : 0))
+      ki = k;
+  if (ki >= 0 && ui >= 0 && ci >= 0 && gen::kShortSplits[ki][ui][ci] > 0)
+    return gen::kShortSplits[ki][ui][ci];
   return decode_splits;
 }
 
 // Prefill tile_splits for a batch without single-token sequences.
 inline int table_prefill_splits(int64_t total_query_tokens, int q_tile, int num_kv_heads,
-                                 int max_context_len) {
+                                 int max_context_len, int head_dim) {
   const int64_t wgs = (total_query_tokens + q_tile - 1) / q_tile * num_kv_heads;
   const int wi = bucket_of(gen::kPfWgBuckets, wgs);
   const int ci = bucket_of(gen::kPfCtxBuckets, max_context_len);
-  if (wi >= 0 && ci >= 0 && gen::kPrefillTileSplits[wi][ci] > 0)
-    return gen::kPrefillTileSplits[wi][ci];
+  int di = -1;
+  constexpr int kDims = sizeof(gen::kPfDims) / sizeof(int);
+  for (int k = 0; k < kDims; ++k)
+    if (gen::kPfDims[k] == head_dim) di = k;
+  if (di >= 0 && wi >= 0 && ci >= 0 && gen::kPrefillTileSplits[di][wi][ci] > 0)
+    return gen::kPrefillTileSplits[di][wi][ci];
   return table_prefill_tile_splits(total_query_tokens, q_tile, num_kv_heads, max_context_len);
 }
 

@@ -180,27 +180,30 @@ def _gen_table(name):
 
 def test_short_run_split_table(lib):
     """Short query runs take their split bound from the short-run table of
-    the generated header, by (units rounded down, context bound rounded up);
-    unswept buckets keep the decode choice."""
+    the generated header, by (head dim, G >= 16) key and (units rounded
+    down, context bound rounded up); unswept buckets keep the decode choice."""
     units_b = _gen_table("kShortUnitBuckets")
     ctx_b = _gen_table("kShortCtxBuckets")
-    table = _gen_table("kShortSplits")
-    assert len(table) == len(units_b) and all(len(r) == len(ctx_b) for r in table)
+    keys = _gen_table("kShortKeys")
+    flat = _gen_table("kShortSplits")
+    assert len(flat) == len(keys) * len(units_b) and all(len(r) == len(ctx_b) for r in flat)
+    table = {tuple(k): flat[i * len(units_b):(i + 1) * len(units_b)] for i, k in enumerate(keys)}
     checked = 0
     for i, units in enumerate(units_b):
         for j, ctx in enumerate(ctx_b):
             blocks = -(-ctx // 16)
-            shapes = [dict(num_q_heads=32, num_kv_heads=1, num_seqs=units,
-                           total_query_tokens=units)]                       # G = 32 decode
+            shapes = [((128, 1), dict(num_q_heads=32, num_kv_heads=1, num_seqs=units,
+                                      total_query_tokens=units))]           # G = 32 decode
             if units >= 8:                                                  # G = 4, 4 tokens
-                shapes.append(dict(num_seqs=units // 8, max_query_len=4,
-                                   total_query_tokens=units // 2))
-            for kw in shapes:
+                shapes.append(((128, 0), dict(num_seqs=units // 8, max_query_len=4,
+                                              total_query_tokens=units // 2)))
+            for key, kw in shapes:
+                want = table[key][i][j]
                 pb = _problem(max_context_len=ctx, max_blocks_per_seq=blocks, **kw)
                 st, t, _ = _select(lib, pb)
                 assert st == pa.PA_OK, kw
-                if table[i][j] > 0:
-                    assert t.num_splits == table[i][j], (units, ctx, kw)
+                if want > 0:
+                    assert t.num_splits == want, (units, ctx, kw)
                     checked += 1
                 # one unit more than the bucket, same context: same bucket
                 kw2 = dict(kw, num_seqs=kw["num_seqs"] + 1,
@@ -209,18 +212,9 @@ def test_short_run_split_table(lib):
                                                   **kw2))
                 next_floor = i + 1 < len(units_b) and (
                     (kw2["num_seqs"] * kw2.get("num_kv_heads", 8)) >= units_b[i + 1])
-                if table[i][j] > 0 and not next_floor:
-                    assert t2.num_splits == table[i][j], (units, ctx, kw2)
+                if want > 0 and not next_floor:
+                    assert t2.num_splits == want, (units, ctx, kw2)
     assert checked > 0
-
-
-@pytest.mark.parametrize("ts", [-1, 9])
-def test_workspace_size_rejects_tile_splits(lib, ts):
-    pb = _problem(max_query_len=64, total_query_tokens=256)
-    t = pa.Tiles(32, 1, 8, 64, 0, ts)
-    ws = ctypes.c_size_t(0)
-    assert lib.pa_workspace_size(ctypes.byref(pb), ctypes.byref(t), ctypes.byref(ws)) == \
-        pa.PA_ERR_INVALID_ARG
 
 
 def test_compute_calls_reject_before_launch(lib):
