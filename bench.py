@@ -35,25 +35,31 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 DECODE_BYTES_PER_TOKEN = 4096
 
-# HBM bytes per decode launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters
-# (scaled by a plain copy of known size), for the kernel as last profiled;
-# None until counters are taken for the current kernel.
+# HBM bytes per call from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (each
+# scaled by what it reads for a plain 256 MiB device copy), for the kernels
+# and launch shapes as last profiled; None where they changed since.
 TRAFFIC = {
-    # decode_kernel<4,8,false> + splitkv_reduce_kernel, num_splits 32
+    # decode_kernel<4,4,false> + splitkv_reduce_kernel, 32 splits
     # (profiles/decode_ctx32k_hbm_counters.md)
-    "decode_ctx32k": 135761419,
-    # decode_even_kernel<4,4> + unit_merge_kernel, num_splits 128
-    # (profiles/decode_b256_ctx8k_kernel_trace.md)
-    "decode_b256_ctx8k": 8604723335,
+    "decode_ctx32k": 135723394,
+    # decode_kernel<4,4,false> + splitkv_reduce_kernel, 8 splits
+    # (profiles/decode_ctx512_hbm_counters.md)
+    "decode_ctx512": 2689164,
+    # decode_even_kernel<4,4> + unit_merge_kernel, split bound 4
+    # (profiles/decode_b64_hbm_counters.md)
+    "decode_b64": 1141094588,
+    # not re-taken for the current launch shape
+    "decode_b256_ctx8k": None,
 }
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {
     # unified_kernel<4,false,128> (profiles/prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 184981238,
-    # unified_kernel<4,false,128> + splitkv_reduce_kernel (profiles/mixed_unified_kernel_trace.md)
-    "mixed_unified": 643112747,
-    # verify_kernel<4,1,false,128> + unit_merge_kernel (profiles/spec_verify_b64_kernel_trace.md)
-    "spec_verify_b64": 1203505088,
+    "prefill_chunk2048": 184926215,
+    # unified_kernel<4,false,128> + splitkv_reduce_kernel
+    # (profiles/mixed_unified_hbm_counters.md)
+    "mixed_unified": 643115110,
+    # not re-taken for the current launch shape
+    "spec_verify_b64": None,
 }
 
 # The same for one pa_cache_append call.
