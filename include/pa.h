@@ -27,8 +27,9 @@
  *                 page*kv_stride_page + slot*kv_stride_token
  *                 + kv_head*kv_stride_head + d   (d stride is 1)
  *                 K and V share the strides.  Default: [pages, P, Hkv, D].
- *                 Each stride must be below 2^31 elements (PA_ERR_UNSUPPORTED
- *                 otherwise).
+ *                 Each stride, and P * kv_stride_token, must be below 2^31
+ *                 elements, and max_blocks_per_seq * P / 16 below 2^31
+ *                 (PA_ERR_UNSUPPORTED otherwise).
  *   block_tables  int32 [B, max_blocks_per_seq]; entry b of row s is the
  *                 page holding logical tokens [b*P, (b+1)*P) of sequence s.
  *                 Entries past ceil(context_lens[s]/P) are never read.
@@ -79,7 +80,7 @@ typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment          */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128/256,
-                             page size != 16, G not in {1,2,4,8,16,32}      */
+                             page size < 16, G not in {1,2,4,8,16,32}       */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
   PA_ERR_HIP = 4          /* a HIP launch failed                            */
 } pa_status;
@@ -92,7 +93,7 @@ typedef struct pa_problem {
   int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads                 */
   int32_t num_kv_heads;       /* Hkv                                            */
   int32_t head_dim;           /* D: 64, 128 or 256 (see PA_ERR_UNSUPPORTED)     */
-  int32_t page_size;          /* P; 16 is built                                 */
+  int32_t page_size;          /* P, a power of two; 16, 32, 64, ... are built   */
   int32_t max_blocks_per_seq; /* row stride of block_tables                     */
   int64_t kv_stride_page;     /* pool strides in elements, multiples of 8       */
   int64_t kv_stride_token;

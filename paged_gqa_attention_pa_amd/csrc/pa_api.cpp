@@ -53,15 +53,24 @@ pa_status check_problem(const pa_problem* pb) {
   if ((int64_t)pb->max_context_len > (int64_t)pb->max_blocks_per_seq * pb->page_size)
     return PA_ERR_INVALID_ARG;
   if ((pb->head_dim != 64 && pb->head_dim != kHeadDim && pb->head_dim != 256) ||
-      pb->page_size != kPage)
+      pb->page_size < kPage)
     return PA_ERR_UNSUPPORTED;
-  // the kernels form page offsets as 32-bit byte strides times page ids
+  // the kernels form page offsets as 32-bit byte strides times page ids, the
+  // slot offsets inside a page in 32 bits, and 16-key tile indices (up to
+  // max_blocks_per_seq * page_size / 16) as int
   if (pb->kv_stride_page > 0x7fffffff || pb->kv_stride_token > 0x7fffffff ||
-      pb->kv_stride_head > 0x7fffffff)
+      pb->kv_stride_head > 0x7fffffff ||
+      (int64_t)pb->kv_stride_token * pb->page_size > 0x7fffffff ||
+      (int64_t)pb->max_blocks_per_seq * (pb->page_size / kPage) > 0x7fffffff)
     return PA_ERR_UNSUPPORTED;
   if (!group_built(pb->num_q_heads / pb->num_kv_heads)) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
+
+// log2 of the page size, and of the 16-key tiles per page (page sizes are
+// powers of two from 16, checked above)
+int log2_page(const pa_problem* pb) { return __builtin_ctz((unsigned)pb->page_size); }
+int page_shift(const pa_problem* pb) { return log2_page(pb) - __builtin_ctz((unsigned)kPage); }
 
 pa_status check_tiles(const pa_tiles* t) {
   if (!t) return PA_ERR_INVALID_ARG;
@@ -201,6 +210,7 @@ pa_status short_runs(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.num_q_heads = problem->num_q_heads;
   d.num_kv_heads = problem->num_kv_heads;
   d.max_blocks = problem->max_blocks_per_seq;
+  d.page_shift = page_shift(problem);
   d.num_splits = S + 1;
   const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
   d.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
@@ -304,6 +314,7 @@ pa_status decode_launch(const pa_problem* problem, const pa_tiles* tiles, const 
   p.num_q_heads = problem->num_q_heads;
   p.num_kv_heads = problem->num_kv_heads;
   p.max_blocks = problem->max_blocks_per_seq;
+  p.page_shift = page_shift(problem);
   p.num_splits = even ? S + 1 : S;
   p.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
   p.max_tiles = ntiles;
@@ -513,6 +524,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   p.num_q_heads = problem->num_q_heads;
   p.num_kv_heads = problem->num_kv_heads;
   p.max_blocks = problem->max_blocks_per_seq;
+  p.page_shift = page_shift(problem);
   p.q_tile = qt;
   p.decode_rows_apart = decode_rows ? 1 : 0;
   p.tile_splits = TS;
@@ -554,6 +566,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   d.num_q_heads = problem->num_q_heads;
   d.num_kv_heads = problem->num_kv_heads;
   d.max_blocks = problem->max_blocks_per_seq;
+  d.page_shift = page_shift(problem);
   d.num_splits = even ? S + 1 : S;
   const int ntiles = ceil_div(problem->max_context_len, pa::kDecodeTile);
   d.tiles_per_split = ntiles > 0 ? ceil_div(ntiles, S) : 1;
@@ -680,6 +693,7 @@ pa_status pa_cache_append(const pa_problem* problem, const void* k_new, const vo
   p.num_seqs = problem->num_seqs;
   p.num_kv_heads = problem->num_kv_heads;
   p.max_blocks = problem->max_blocks_per_seq;
+  p.log2_page = log2_page(problem);
   p.total_tokens = problem->total_query_tokens;
   p.head_dim = problem->head_dim;
   return from_hip(pa::launch_append(p, stream));
@@ -701,6 +715,7 @@ pa_status pa_check_inputs(const pa_problem* problem, int64_t num_pages,
   p.num_pages = num_pages;
   p.num_seqs = problem->num_seqs;
   p.max_blocks = problem->max_blocks_per_seq;
+  p.log2_page = log2_page(problem);
   p.max_context_len = problem->max_context_len;
   p.max_query_len = query_start_loc ? problem->max_query_len : 1;
   p.total_tokens = problem->total_query_tokens;

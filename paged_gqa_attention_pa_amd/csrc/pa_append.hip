@@ -49,10 +49,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
   // Undefined input (a row past the sequence's tokens, a context shorter than
   // its new tokens, a position past the table row, a padded table entry):
   // nothing is written, so a bad batch cannot write outside the pools.
-  if (i >= qlen || pos < 0 || pos / kPage >= p.max_blocks) return;
-  const int64_t page = p.block_tables[(int64_t)s * p.max_blocks + pos / kPage];
+  if (i >= qlen || pos < 0 || (pos >> p.log2_page) >= p.max_blocks) return;
+  const int64_t page = p.block_tables[(int64_t)s * p.max_blocks + (pos >> p.log2_page)];
   if (page < 0) return;
-  const int64_t dst = page * p.stride_page + (int64_t)(pos % kPage) * p.stride_token +
+  const int64_t dst = page * p.stride_page +
+                      (int64_t)(pos & ((1 << p.log2_page) - 1)) * p.stride_token +
                       (int64_t)h * p.stride_head + 8 * dc;
   const int64_t src = row * D + 8 * dc;
   const u32x4 k = *reinterpret_cast<const u32x4*>(p.k_new + src);

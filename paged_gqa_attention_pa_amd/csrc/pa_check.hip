@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckParams p) {
   const int s = blockIdx.x / p.chunks;
   const int c = blockIdx.x % p.chunks;
   const int L = p.context_lens[s];
-  const int64_t nblk = L > 0 ? ((int64_t)L + kPage - 1) / kPage : 0;
+  const int64_t nblk = L > 0 ? (((int64_t)L - 1) >> p.log2_page) + 1 : 0;
   const int64_t used = nblk < p.max_blocks ? nblk : p.max_blocks;
   int32_t bits = 0;
   const int64_t idx = (int64_t)c * kCheckThreads + threadIdx.x;

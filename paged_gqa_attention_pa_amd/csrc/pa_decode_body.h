@@ -114,16 +114,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   bf16x8 qb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(ld16(qrow + 32 * j + 8 * c));
+  // 16-key tile t lies in block-table entry t >> page_shift, 16 * (t & pmask)
+  // slots into that page
   const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
+  const int ps = p.page_shift, pmask = (1 << p.page_shift) - 1;
+  const int tok16 = 16 * (int)p.stride_token;  // < 2^31: a page spans < 2^31 elements
   const int t_first = t_begin + wave + W * lane;
-  int pages = (t_first < p.max_blocks) ? bt[t_first] : 0;
+  int pages = ((t_first >> ps) < p.max_blocks) ? bt[t_first >> ps] : 0;
 
   const int L = p.context_lens[b];
   // A context beyond the host bound is undefined behaviour; clamping here only
   // keeps every access inside the block table and the workspace.
   const int ntiles = EVEN ? ev.t_end
                         : min((L + kDecodeTile - 1) / kDecodeTile,
-                              min(p.max_blocks, p.num_splits * tps));
+                              min(p.max_blocks << ps, p.num_splits * tps));
   const int n_act = EVEN ? 1 : (ntiles + tps - 1) / tps;  // non-empty splits of this sequence
   if (!EVEN && split >= (n_act > 1 ? n_act : 1)) {
     // Unfused merge: the separate reduce reads every split, so an empty one
@@ -144,12 +148,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   // this wave's tile chunk*64 + i.
   auto fetch_pages = [&](int chunk) {
     const int i = lane + 64 * chunk;
-    pages = (i < nt) ? bt[t_begin + wave + W * i] : 0;
+    pages = (i < nt) ? bt[(t_begin + wave + W * i) >> ps] : 0;
   };
+  int chunk_base = 0;  // first tile index (of this wave's list) of the current chunk
   auto issue = [&](int i, uint4 (&kr)[4], uint4 (&vr)[4]) {
     const int64_t page = readlane(pages, i & 63);
-    const uint16_t* kp = kbase + page * p.stride_page;
-    const uint16_t* vp = vbase + page * p.stride_page;
+    const int t = t_begin + wave + W * (chunk_base + i);
+    const int64_t off = page * p.stride_page + (int64_t)((t & pmask) * tok16);
+    const uint16_t* kp = kbase + off;
+    const uint16_t* vp = vbase + off;
 #pragma unroll
     for (int j = 0; j < 4; ++j) kr[j] = ld16(kp + 32 * j);
 #pragma unroll
@@ -230,6 +237,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   // of draining every outstanding load.
   for (int cb = 0; cb < nt; cb += 64) {
     const int n = min(64, nt - cb);
+    chunk_base = cb;
     if (cb > 0) fetch_pages(cb >> 6);
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) issue(min(d, n - 1), kr[d], vr[d]);

@@ -41,7 +41,7 @@ __device__ void decode_even_body(const DecodeParams& p, int w, int nw, float* sm
       if (qn <= 0 || qn * G > 16 * RB) return 0;
     }
     const int L = p.context_lens[b];
-    return min((L + kDecodeTile - 1) / kDecodeTile, min(p.max_blocks, p.max_tiles));
+    return min((L + kDecodeTile - 1) / kDecodeTile, min(p.max_blocks << p.page_shift, p.max_tiles));
   };
   // Pass 1: total tiles.
   long long tot = 0;

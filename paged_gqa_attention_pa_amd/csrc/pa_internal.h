@@ -9,7 +9,7 @@
 namespace pa {
 
 constexpr int kHeadDim = 128;   // built head dimension
-constexpr int kPage = 16;       // built page size
+constexpr int kPage = 16;       // keys per block of the prefill page window; smallest page size
 constexpr int kDecodeTile = 16; // keys per decode step (one MFMA N-tile)
 constexpr int kMaxSplits = 256;        // decode split-KV
 constexpr int kReduceMaxSplits = 4096; // pa_splitkv_reduce
@@ -38,6 +38,7 @@ struct DecodeParams {
   const int32_t* query_start_loc;  // mixed batch: [B+1]; null for a pure decode batch
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
+  int32_t page_shift;       // log2(page_size / 16): 16-key tiles per page = 1 << page_shift
   int32_t tiles_per_split;  // 16-key tiles per split
   int32_t num_splits;       // partial slots per row (even-work grid: splits + 1)
   int32_t max_tiles;        // ceil(max_context_len / 16): bound on a unit's tiles
@@ -59,6 +60,7 @@ struct PrefillParams {
   float* lse;               // [T, Hq] or null
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks;
+  int32_t page_shift;       // log2(page_size / 16)
   int32_t q_tile;           // query tokens per workgroup
   int32_t decode_rows_apart;  // 1: single-token sequences run as decode workgroups
   // tile_splits > 1: each query tile's key range is cut into that many runs
@@ -119,6 +121,7 @@ struct AppendParams {
   int64_t stride_page, stride_token, stride_head;
   int32_t num_seqs, num_kv_heads, max_blocks, total_tokens;
   int32_t head_dim;         // 64, 128 or 256
+  int32_t log2_page;        // log2(page_size)
 };
 
 // Launchers: return hipSuccess or the launch error.  Shapes were checked.
@@ -151,6 +154,7 @@ struct CheckParams {
   int32_t* flags;                  // device int32, PA_CHECK_* bits
   int64_t num_pages;
   int32_t num_seqs, max_blocks, max_context_len, max_query_len, total_tokens;
+  int32_t log2_page;               // log2(page_size)
   int32_t chunks;                  // ceil(max_blocks / 256): workgroups per sequence
 };
 // Clears *flags, then ORs in the PA_CHECK_* bit of every failed check.

@@ -68,7 +68,8 @@ constexpr int v_stride() {
 }
 constexpr int kKBufs = 4;                 // LDS K tile buffers
 constexpr int kVBufs = 5;                 // LDS V tile buffers (V is read one step later)
-// block-table entries staged in LDS: 2048 (32k keys), 1024 (16k keys) at 256
+// 16-key blocks of the LDS page window (one 64-bit byte offset each): 2048
+// (32k keys), 1024 (16k keys) at head dim 256
 template <int D>
 constexpr int page_cache() {
   return D == 256 ? 1024 : 2048;
@@ -123,11 +124,12 @@ __device__ bool find_tile(const int32_t* qsl, int num_seqs, int qt, int x, bool 
   return s_found[0] >= 0;
 }
 
-// LDS bytes prefill_body needs from its caller (K tiles, V^T tiles, page ids).
+// LDS bytes prefill_body needs from its caller (K tiles, V^T tiles, the
+// page window's block offsets).
 template <int D = kHeadDim>
 constexpr int prefill_smem_bytes() {
   return kKBufs * kKvTile * k_stride<D>() * 2 + kVBufs * kKvTile * v_stride<D>() * 2 +
-         page_cache<D>() * 4;
+         page_cache<D>() * 8;
 }
 
 // One workgroup of 64 * waves_of<D>() threads: query tile / split / KV head
@@ -228,33 +230,34 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   // multi-chunk staging: the odd chunks sit KSTEP slots further into a page
   const uint32_t odd_bytes = (uint32_t)(KSTEP * p.stride_token * 2);
   const uint32_t page_bytes = (uint32_t)(p.stride_page * 2);  // < 2^32 (checked on the host)
-  // Page ids of the current window of key tiles, staged in LDS, keep the
-  // block-table lookup off each tile's load path.  Entries past the
-  // context hold page 0 (never used: those keys are masked and zeroed).
-  int* pg_lds = reinterpret_cast<int*>(smem + kKBufs * kKvTile * kLdsStride * 2 +
-                                       kVBufs * kKvTile * kVStride * 2);
+  // Byte offsets of the 16-key blocks of the current window of key tiles
+  // (block j: page bt[j >> page_shift], slots 16 * (j & pmask) ..), staged in
+  // LDS, keep the block-table lookup and the address arithmetic off each
+  // tile's load path.  Blocks past the context hold offset 0 (page 0, never
+  // used: those keys are masked and zeroed).
+  uint64_t* pg_lds = reinterpret_cast<uint64_t*>(smem + kKBufs * kKvTile * kLdsStride * 2 +
+                                                 kVBufs * kKvTile * kVStride * 2);
   constexpr int kWinTiles = page_cache<D>() * kPage / kKvTile;
-  const int nblk = (L + kPage - 1) / kPage;  // valid block-table entries
+  const int ps = p.page_shift, pmask = (1 << p.page_shift) - 1;
+  const uint32_t block_bytes = (uint32_t)(kPage * p.stride_token * 2);  // 16 slots of a page
+  // valid 16-key blocks: inside the context and the block table
+  const int nblk = min((L + kPage - 1) / kPage, p.max_blocks << ps);
   int win0 = 0;                              // first key tile of the window
   // tile t of the window -> r[i] = K chunk i, r[NC + i] = V chunk i (split:
   // r[0] = this thread's K or V chunk)
   constexpr int NR = kSplitKV ? 1 : 2 * NC;
   auto load_tile = [&](int t, uint4 (&r)[NR]) {
     if constexpr (kSplitKV) {
-      const uint64_t off =
-          (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + lkey / kPage] * page_bytes;
+      const uint64_t off = pg_lds[t * (kKvTile / kPage) + lkey / kPage];
       r[0] = *reinterpret_cast<const uint4*>((stage_v ? vth : kth) + off);
     } else if constexpr (NC == 1) {
-      const uint64_t off =
-          (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + lkey / kPage] * page_bytes;
+      const uint64_t off = pg_lds[t * (kKvTile / kPage) + lkey / kPage];
       r[0] = *reinterpret_cast<const uint4*>(kth + off);
       r[1] = *reinterpret_cast<const uint4*>(vth + off);
     } else {
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        const uint64_t off =
-            (uint64_t)(uint32_t)pg_lds[t * (kKvTile / kPage) + i / 2] * page_bytes +
-            ((i & 1) ? odd_bytes : 0u);
+        const uint64_t off = pg_lds[t * (kKvTile / kPage) + i / 2] + ((i & 1) ? odd_bytes : 0u);
         r[i] = *reinterpret_cast<const uint4*>(kth + off);
         r[NC + i] = *reinterpret_cast<const uint4*>(vth + off);
       }
@@ -456,7 +459,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
     {
       const int b0 = win0 * (kKvTile / kPage);
       const int nb = nw * (kKvTile / kPage);
-      for (int i = tid; i < nb; i += T) pg_lds[i] = (b0 + i < nblk) ? bt[b0 + i] : 0;
+      for (int i = tid; i < nb; i += T) {
+        const int j = b0 + i;
+        pg_lds[i] = (j < nblk) ? (uint64_t)(uint32_t)bt[j >> ps] * page_bytes +
+                                     (uint64_t)((j & pmask) * block_bytes)
+                               : 0ull;
+      }
       __syncthreads();
     }
     // the first three tiles' loads are all issued before any is stored, so

@@ -109,9 +109,13 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
     }
   }
   const int t_begin = ev.t_begin;
+  // 16-key tile t lies in block-table entry t >> page_shift, 16 * (t & pmask)
+  // slots into that page
   const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
+  const int ps = p.page_shift, pmask = (1 << p.page_shift) - 1;
+  const int tok16 = 16 * (int)p.stride_token;  // < 2^31: a page spans < 2^31 elements
   const int t_first = t_begin + strm + WS * lane;
-  int pages = (t_first < p.max_blocks) ? bt[t_first] : 0;
+  int pages = ((t_first >> ps) < p.max_blocks) ? bt[t_first >> ps] : 0;
 
   const int L = p.context_lens[b];
   const int t_end = ev.t_end;
@@ -139,12 +143,15 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
 
   auto fetch_pages = [&](int chunk) {
     const int i = lane + 64 * chunk;
-    pages = (i < nt) ? bt[t_begin + strm + WS * i] : 0;
+    pages = (i < nt) ? bt[(t_begin + strm + WS * i) >> ps] : 0;
   };
+  int chunk_base = 0;  // first tile index (of this stream's list) of the current chunk
   auto issue = [&](int i, uint4 (&kr)[KS], uint4 (&vr)[NV]) {
     const int64_t page = readlane(pages, i & 63);
-    const uint16_t* kp = kbase + page * p.stride_page;
-    const uint16_t* vp = vbase + page * p.stride_page;
+    const int t = t_begin + strm + WS * (chunk_base + i);
+    const int64_t off = page * p.stride_page + (int64_t)((t & pmask) * tok16);
+    const uint16_t* kp = kbase + off;
+    const uint16_t* vp = vbase + off;
 #pragma unroll
     for (int j = 0; j < KS; ++j) kr[j] = ld16(kp + 32 * j);
 #pragma unroll
@@ -251,6 +258,7 @@ __device__ __forceinline__ void verify_body(const DecodeParams& p, int g, int b,
   // chunk in ring slot i % DEPTH, no load under a branch.
   for (int cb = 0; cb < nt; cb += 64) {
     const int nc = min(64, nt - cb);
+    chunk_base = cb;
     if (cb > 0) fetch_pages(cb >> 6);
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) issue(min(d, nc - 1), kr[d], vr[d]);

@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <vector>
 
 #include "../paged_gqa_attention_pa_amd/csrc/pa_even_plan.h"
@@ -56,7 +57,11 @@ int main(int argc, char** argv) {
     }
     max_ctx += uniform(0, 100);  // the host bound may exceed every length
     const int max_tiles = (max_ctx + 15) / 16;
-    const int max_blocks = max_tiles + uniform(0, 3);
+    // pages of 16 << ps slots; the table may hold more entries than needed,
+    // or (a context past the table, which the input checks report) fewer
+    const int ps = uniform(0, 3) == 0 ? uniform(1, 6) : 0;
+    const int need = (max_tiles + (1 << ps) - 1) >> ps;
+    const int max_blocks = std::max(1, need + uniform(-1, 3));
     const long long min_tiles = max_tiles > 0 ? (max_tiles + S - 1) / S : 1;
     const int slots = S + 1;
     // tiles per sequence, as the kernels clamp them
@@ -64,7 +69,7 @@ int main(int argc, char** argv) {
     long long per_head = 0;
     for (int b = 0; b < B; ++b) {
       const int t = (L[b] + 15) / 16;
-      const int cap = max_blocks < max_tiles ? max_blocks : max_tiles;
+      const int cap = (max_blocks << ps) < max_tiles ? (max_blocks << ps) : max_tiles;
       nt[b] = t < cap ? t : cap;
       per_head += nt[b];
     }

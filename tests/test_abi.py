@@ -82,8 +82,10 @@ def test_select_tiles_decode_and_prefill(lib):
     ("num_q_heads", 30, pa.PA_ERR_INVALID_ARG),       # Hq % Hkv != 0
     ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
     ("page_size", 12, pa.PA_ERR_INVALID_ARG),         # not a power of two
-    ("page_size", 32, pa.PA_ERR_UNSUPPORTED),
+    ("page_size", 0, pa.PA_ERR_INVALID_ARG),
     ("kv_stride_token", 1020, pa.PA_ERR_INVALID_ARG),  # not a multiple of 8
+    # a page's slots span 2^31 elements or more
+    ("kv_stride_token", 1 << 27, pa.PA_ERR_UNSUPPORTED),
     ("max_context_len", 512 * 16 + 1, pa.PA_ERR_INVALID_ARG),
     ("num_seqs", -1, pa.PA_ERR_INVALID_ARG),
     ("out_dtype", 7, pa.PA_ERR_INVALID_ARG),
@@ -96,6 +98,27 @@ def test_select_tiles_decode_and_prefill(lib):
 def test_select_tiles_rejects(lib, field, value, status):
     st, _, _ = _select(lib, _problem(**{field: value}))
     assert st == status
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 64, 128, 256, 1024])
+def test_page_sizes_accepted(lib, page_size):
+    """Pages of any power of two from 16 slots: a page is 2^k 16-key tiles."""
+    st, t, ws = _select(lib, _problem(page_size=page_size, kv_stride_page=page_size * 8 * 128))
+    assert st == pa.PA_OK and t.num_splits >= 1 and ws > 0
+
+
+def test_page_size_below_one_tile(lib):
+    st, _, _ = _select(lib, _problem(page_size=8, max_blocks_per_seq=1024))
+    assert st == pa.PA_ERR_UNSUPPORTED
+
+
+def test_page_tile_index_bound(lib):
+    """16-key tile indices of a table row (max_blocks_per_seq * P / 16) must fit in int."""
+    big = dict(page_size=1024, kv_stride_page=1024 * 8 * 128)
+    st, _, _ = _select(lib, _problem(max_blocks_per_seq=(1 << 31) // 64 - 1, **big))
+    assert st == pa.PA_OK
+    st, _, _ = _select(lib, _problem(max_blocks_per_seq=(1 << 31) // 64, **big))
+    assert st == pa.PA_ERR_UNSUPPORTED
 
 
 def test_group_sizes_built(lib):
@@ -283,7 +306,7 @@ def test_cache_append_rejects_before_launch(lib):
     # one token per sequence unless query_start_loc is given
     assert call(_problem(total_query_tokens=9)) == pa.PA_ERR_INVALID_ARG
     assert call(_problem(head_dim=96, kv_stride_head=96)) == pa.PA_ERR_UNSUPPORTED
-    assert call(_problem(page_size=32)) == pa.PA_ERR_UNSUPPORTED
+    assert call(_problem(page_size=8, max_blocks_per_seq=1024)) == pa.PA_ERR_UNSUPPORTED
     assert call(_problem(kv_stride_token=12)) == pa.PA_ERR_INVALID_ARG
     # nothing to write: no launch
     assert call(_problem(num_seqs=0, total_query_tokens=0)) == pa.PA_OK
