@@ -1,7 +1,8 @@
 // Paged GQA decode body (split-KV), for gfx950.
 //
 // One workgroup = (split, kv head, sequence); its W wavefronts stream the
-// split's 16-key tiles (tile t = page t, page size 16) round-robin, each with
+// split's 16-key tiles round-robin (with pages of P = 16 * 2^s slots, tile t
+// is slots 16 * (t mod 2^s) .. + 15 of block-table entry t >> s), each with
 // its own online-softmax state, and merge through LDS at the end.
 //
 // Per tile and wavefront:

@@ -1,12 +1,13 @@
 // Paged GQA prefill body (bf16 MFMA) for gfx950.
 //
 // One workgroup = (query tile of one sequence, kv head).  Its Q-block is
-// 256 rows: QT = 256 / G query tokens x the G query heads that share the KV
-// head (the Q-Block step of the IBM Triton summary's five-step list), row
-// r -> token r / G, head r % G; wavefront w owns rows 32w..32w+31 and each
-// lane owns one row (lane % 32).  The workgroup walks the sequence's keys in
-// tiles of 32 (two pages), up to the causal limit of its last token, staging
-// each K and V tile in LDS once for all eight wavefronts (FlashAttention-style
+// 256 rows (128 at head dim 256): QT = rows / G query tokens x the G query
+// heads that share the KV head (the Q-Block step of the IBM Triton summary's
+// five-step list), row r -> token r / G, head r % G; wavefront w owns rows
+// 32w..32w+31 and each lane owns one row (lane % 32).  The workgroup walks
+// the sequence's keys in tiles of 32 (two 16-slot blocks of its pages), up
+// to the causal limit of its last token, staging each K and V tile in LDS
+// once for all its wavefronts (FlashAttention-style
 // tiling, guide sections "Flash Attention革命" and "Triton实现Flash
 // Attention"):
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, K rows from LDS (16-byte reads),

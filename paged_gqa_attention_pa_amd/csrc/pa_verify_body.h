@@ -6,7 +6,7 @@
 // and the whole of it is one Q-block (the Q-Block step of the same summary's
 // five-step list, stretched over tokens as well as heads): K and V are read
 // once for all R rows.  The work split is the decode one: W wavefronts take
-// a piece's 16-key tiles (one page each) round-robin, each with its own
+// a piece's 16-key tiles (16 slots of a page each) round-robin, each with its own
 // online-softmax state, and merge through LDS at the end.
 //
 // Per tile and wavefront:
