@@ -72,6 +72,182 @@ constexpr int decode_smem_floats() {
   return W * G * D > merge ? W * G * D : merge;
 }
 
+// The B operand: the G query heads of KV head g for query row qi (column n
+// takes head n % G), 16 bytes of each of the four 32-dim k-steps per lane.
+template <int G>
+__device__ __forceinline__ void load_q_block(const DecodeParams& p, int qi, int g, int hl, int c,
+                                             bf16x8 (&qb)[4]) {
+  const uint16_t* qrow = p.q + ((int64_t)qi * p.num_q_heads + g * G + hl) * kHeadDim;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(ld16(qrow + 32 * j + 8 * c));
+}
+
+// Lane byte offsets inside a (page, kv head) slice: K chunk of MFMA row n
+// (key sigma(n), dims 8c..), V row chunk (key c, dims 8n..).  Below 2^31: a
+// page spans fewer than 2^31 elements.
+__device__ __forceinline__ uint32_t k_lane_offset(const DecodeParams& p, int c, int n) {
+  const int ktok = (n >> 2) + 4 * (n & 3);  // sigma: MFMA row -> key in tile
+  return (uint32_t)(2 * (ktok * (int)p.stride_token + 8 * c));
+}
+__device__ __forceinline__ uint32_t v_lane_offset(const DecodeParams& p, int c, int n) {
+  return (uint32_t)(2 * (c * (int)p.stride_token + 8 * n));
+}
+
+// K and V of 16-key tile t of KV head g, whose block-table entry names
+// `page`, into one ring slot: four 16-byte K chunks (the MFMA A operand)
+// and four V rows of 16 bytes per lane.  The tile's base address is uniform
+// (page, head and slot are the same on every lane), the lane offsets koff /
+// voff are 32-bit, so each load is a scalar base plus a vector offset.
+__device__ __forceinline__ void load_kv_tile(const DecodeParams& p, int g, int64_t page, int t,
+                                             int pmask, int tok16, uint32_t koff, uint32_t voff,
+                                             uint4 (&kr)[4], uint4 (&vr)[4]) {
+  const int64_t off = page * p.stride_page + (int64_t)g * p.stride_head +
+                      (int64_t)((t & pmask) * tok16);
+  const char* kb = reinterpret_cast<const char*>(p.k_pool + off);
+  const char* vb = reinterpret_cast<const char*>(p.v_pool + off);
+  const int64_t vrow = 8 * p.stride_token;  // bytes between V rows 4 keys apart
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kr[j] = *reinterpret_cast<const uint4*>(kb + koff + 64 * j);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vr[r] = *reinterpret_cast<const uint4*>((vb + r * vrow) + voff);
+}
+
+// One tile of one wavefront: the scores of keys 16t.. (those at or past L
+// masked), the online-softmax update of (m, lsum, acc), and P.V.
+template <int G>
+__device__ __forceinline__ void tile_update(const DecodeParams& p, const uint4 (&kc)[4],
+                                            uint4 (&vc)[4], const bf16x8 (&qb)[4], int t, int L,
+                                            int c, int lane, float& m, float& lsum,
+                                            float (&acc)[G][8]) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[j]), qb[j], s, 0, 0, 0);
+
+  const int key0 = t * kDecodeTile + c;
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (key0 + 4 * r < L) ? s[r] * p.scale_log2 : kNegInf;
+  float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+
+  const bool need = tmax > m + kLazyThreshold;
+  if (wave_any(need)) {
+    const float m_new = need ? tmax : m;
+    const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
+    m = m_new;
+    lsum *= alpha;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ah = head_bcast<G>(alpha, h, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
+    }
+  }
+
+  float pr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(x[r] - m);
+  lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+  if (t * kDecodeTile + kDecodeTile > L) {  // last tile: drop stale V rows
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (key0 + 4 * r >= L) vc[r] = make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float v[8];
+    v[0] = bf16lo(vc[r].x); v[1] = bf16hi(vc[r].x);
+    v[2] = bf16lo(vc[r].y); v[3] = bf16hi(vc[r].y);
+    v[4] = bf16lo(vc[r].z); v[5] = bf16hi(vc[r].z);
+    v[6] = bf16lo(vc[r].w); v[7] = bf16hi(vc[r].w);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ph = head_bcast<G>(pr[r], h, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+    }
+  }
+}
+
+// End of one (sequence, kv head) unit or piece of it: sum each wavefront's
+// state over its four key groups, merge the W wavefronts through LDS and
+// write the G rows, to the output (direct) or as normalised partials with
+// their lse to slot `slot` of S (partial rows are per sequence, b * Hq + h).
+// Ends with the LDS buffer still in use: callers that reuse it synchronise.
+template <int G, int W>
+__device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, float (&acc)[G][8],
+                                                      float m, float lsum, int b, int g, int qi,
+                                                      bool direct, int S, int slot,
+                                                      float* sm_buf) {
+  constexpr int D = kHeadDim;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane >> 4, n = lane & 15;
+  // Sum this wavefront's partials over the four key groups.
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[h][e] += shfl_xor(acc[h][e], 16);
+      acc[h][e] += shfl_xor(acc[h][e], 32);
+    }
+
+  // Merge the W wavefronts through LDS.
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+  if (c == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&sm_buf[(wave * G + h) * D + 8 * n]);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+    if (n < G) {
+      sm_m[wave][n] = m;
+      sm_l[wave][n] = lsum;
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < G * D; idx += 64 * W) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
+    float o = 0.f, l = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = sm_m[w][h];
+        if (mw != kNegInf) {
+          const float e = fast_exp2(mw - M);
+          o = fmaf(e, sm_buf[(w * G + h) * D + d], o);
+          l = fmaf(e, sm_l[w][h], l);
+        }
+      }
+      o = o / l;
+    }
+    const float lse_nat = (M == kNegInf) ? kNegInf : (M + fast_log2(l)) * kLn2;
+    const int64_t row = (int64_t)b * p.num_q_heads + g * G + h;  // partials: per sequence
+    if (direct) {
+      const int64_t orow = (int64_t)qi * p.num_q_heads + g * G + h;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[orow * D + d] = o;
+      else
+        reinterpret_cast<uint16_t*>(p.out)[orow * D + d] = f2bf(o);
+      if (p.lse && d == 0) p.lse[orow] = lse_nat;
+    } else {
+      p.part_o[(row * S + slot) * D + d] = o;
+      if (d == 0) p.part_lse[row * S + slot] = lse_nat;
+    }
+  }
+}
+
 // Where a piece of one (sequence, kv head) unit goes in the even-work grid:
 // tiles [t_begin, t_end), written straight to the output when the piece is
 // the whole unit, else to partial slot `slot` of `slots`.
@@ -111,10 +287,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   // split*tps + wave + W*i, read only inside the block-table row).
   const int tps = p.tiles_per_split;
   const int t_begin = EVEN ? ev.t_begin : split * tps;
-  const uint16_t* qrow = p.q + ((int64_t)qi * p.num_q_heads + g * G + hl) * D;
   bf16x8 qb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) qb[j] = as_bf16x8(ld16(qrow + 32 * j + 8 * c));
+  load_q_block<G>(p, qi, g, hl, c, qb);
   // 16-key tile t lies in block-table entry t >> page_shift, 16 * (t & pmask)
   // slots into that page
   const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks;
@@ -141,9 +315,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   // tiles of this wavefront: t_begin + wave + W*i, i < nt
   const int nt = (t_end - t_begin - wave + W - 1) / W > 0 ? (t_end - t_begin - wave + W - 1) / W : 0;
 
-  const int ktok = (n >> 2) + 4 * (n & 3);  // sigma: MFMA row -> key in tile
-  const uint16_t* kbase = p.k_pool + (int64_t)g * p.stride_head + (int64_t)ktok * p.stride_token + 8 * c;
-  const uint16_t* vbase = p.v_pool + (int64_t)g * p.stride_head + (int64_t)c * p.stride_token + 8 * n;
+  const uint32_t koff = k_lane_offset(p, c, n), voff = v_lane_offset(p, c, n);
 
   // Page ids of later chunks, 64 tiles at a time: lane i holds the page of
   // this wave's tile chunk*64 + i.
@@ -153,15 +325,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   };
   int chunk_base = 0;  // first tile index (of this wave's list) of the current chunk
   auto issue = [&](int i, uint4 (&kr)[4], uint4 (&vr)[4]) {
-    const int64_t page = readlane(pages, i & 63);
-    const int t = t_begin + wave + W * (chunk_base + i);
-    const int64_t off = page * p.stride_page + (int64_t)((t & pmask) * tok16);
-    const uint16_t* kp = kbase + off;
-    const uint16_t* vp = vbase + off;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kr[j] = ld16(kp + 32 * j);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = ld16(vp + (int64_t)(4 * r) * p.stride_token);
+    load_kv_tile(p, g, readlane(pages, i & 63), t_begin + wave + W * (chunk_base + i), pmask,
+                 tok16, koff, voff, kr, vr);
   };
 
   float acc[G][8];
@@ -175,59 +340,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
   uint4 kr[DEPTH][4], vr[DEPTH][4];
 
   auto process = [&](uint4 (&kc)[4], uint4 (&vc)[4], int i) {
-    const int t = t_begin + wave + W * i;
-
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[j]), qb[j], s, 0, 0, 0);
-
-    const int key0 = t * kDecodeTile + c;
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (key0 + 4 * r < L) ? s[r] * p.scale_log2 : kNegInf;
-    float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-
-    const bool need = tmax > m + kLazyThreshold;
-    if (wave_any(need)) {
-      const float m_new = need ? tmax : m;
-      const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
-      m = m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ah = head_bcast<G>(alpha, h, lane);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
-      }
-    }
-
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(x[r] - m);
-    lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-
-    if (t * kDecodeTile + kDecodeTile > L) {  // last tile: drop stale V rows
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (key0 + 4 * r >= L) vc[r] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v[8];
-      v[0] = bf16lo(vc[r].x); v[1] = bf16hi(vc[r].x);
-      v[2] = bf16lo(vc[r].y); v[3] = bf16hi(vc[r].y);
-      v[4] = bf16lo(vc[r].z); v[5] = bf16hi(vc[r].z);
-      v[6] = bf16lo(vc[r].w); v[7] = bf16hi(vc[r].w);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ph = head_bcast<G>(pr[r], h, lane);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
-      }
-    }
+    tile_update<G>(p, kc, vc, qb, t_begin + wave + W * i, L, c, lane, m, lsum, acc);
   };
 
   // Software pipeline over chunks of 64 tiles.  Tile i of a chunk lives in
@@ -256,72 +369,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int split, in
       if (i0 + d < n) process(kr[d], vr[d], cb + i0 + d);
   }
 
-  // Sum this wavefront's partials over the four key groups.
-  lsum += shfl_xor(lsum, 16);
-  lsum += shfl_xor(lsum, 32);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[h][e] += shfl_xor(acc[h][e], 16);
-      acc[h][e] += shfl_xor(acc[h][e], 32);
-    }
-
-  // Merge the W wavefronts through LDS.
-  __shared__ float sm_m[W][G];
-  __shared__ float sm_l[W][G];
   __shared__ float sm_head[2][G];
   __shared__ int sm_last;
-  if (c == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float4* dst = reinterpret_cast<float4*>(&sm_buf[(wave * G + h) * D + 8 * n]);
-      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
-    if (n < G) {
-      sm_m[wave][n] = m;
-      sm_l[wave][n] = lsum;
-    }
-  }
-  __syncthreads();
-
   const int S = EVEN ? ev.slots : p.num_splits;
   const int slot = EVEN ? ev.slot : split;
   const bool direct = EVEN ? ev.direct : (FUSED ? n_act <= 1 : S == 1);
-  for (int idx = tid; idx < G * D; idx += 64 * W) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
-    float o = 0.f, l = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float mw = sm_m[w][h];
-        if (mw != kNegInf) {
-          const float e = fast_exp2(mw - M);
-          o = fmaf(e, sm_buf[(w * G + h) * D + d], o);
-          l = fmaf(e, sm_l[w][h], l);
-        }
-      }
-      o = o / l;
-    }
-    const float lse_nat = (M == kNegInf) ? kNegInf : (M + fast_log2(l)) * kLn2;
-    const int64_t row = (int64_t)b * p.num_q_heads + g * G + h;  // partials: per sequence
-    if (direct) {
-      const int64_t orow = (int64_t)qi * p.num_q_heads + g * G + h;
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.out)[orow * D + d] = o;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[orow * D + d] = f2bf(o);
-      if (p.lse && d == 0) p.lse[orow] = lse_nat;
-    } else {
-      p.part_o[(row * S + slot) * D + d] = o;
-      if (d == 0) p.part_lse[row * S + slot] = lse_nat;
-    }
-  }
+  merge_waves_and_store<G, W>(p, acc, m, lsum, b, g, qi, direct, S, slot, sm_buf);
   if (direct || !FUSED) return;
 
   // Split-KV: count this split in; the last one merges.  The barrier makes
