@@ -41,23 +41,23 @@ DECODE_BYTES_PER_TOKEN = 4096
 TRAFFIC = {
     # decode_kernel<4,4,false> + splitkv_reduce_kernel, 32 splits
     # (profiles/decode_ctx32k_hbm_counters.md)
-    "decode_ctx32k": 135723394,
+    "decode_ctx32k": 135727485,
     # decode_kernel<4,4,false> + splitkv_reduce_kernel, 8 splits
     # (profiles/decode_ctx512_hbm_counters.md)
-    "decode_ctx512": 2689164,
+    "decode_ctx512": 2691226,
     # decode_even_kernel<4,4> + unit_merge_kernel, split bound 4
     # (profiles/decode_b64_hbm_counters.md)
-    "decode_b64": 1141094588,
+    "decode_b64": 1141207279,
     # not re-taken for the current launch shape
     "decode_b256_ctx8k": None,
 }
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {
     # unified_kernel<4,false,128> (profiles/prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 184926215,
+    "prefill_chunk2048": 184974034,
     # unified_kernel<4,false,128> + splitkv_reduce_kernel
     # (profiles/mixed_unified_hbm_counters.md)
-    "mixed_unified": 643115110,
+    "mixed_unified": 643195419,
     # not re-taken for the current launch shape
     "spec_verify_b64": None,
 }
@@ -65,7 +65,7 @@ PREFILL_TRAFFIC = {
 # The same for one pa_cache_append call.
 APPEND_TRAFFIC = {
     # append_kernel (profiles/append_prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 67204233,
+    "prefill_chunk2048": 67206941,
 }
 
 
