@@ -48,8 +48,9 @@ TRAFFIC = {
     # decode_even_kernel<4,4> + unit_merge_kernel, split bound 4
     # (profiles/decode_b64_hbm_counters.md)
     "decode_b64": 1141207279,
-    # not re-taken for the current launch shape
-    "decode_b256_ctx8k": None,
+    # decode_even_kernel<4,8> + unit_merge_kernel, split bound 128
+    # (profiles/decode_b256_ctx8k_hbm_counters.md)
+    "decode_b256_ctx8k": 8598464767,
 }
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {
@@ -58,8 +59,9 @@ PREFILL_TRAFFIC = {
     # unified_kernel<4,false,128> + splitkv_reduce_kernel
     # (profiles/mixed_unified_hbm_counters.md)
     "mixed_unified": 643195419,
-    # not re-taken for the current launch shape
-    "spec_verify_b64": None,
+    # verify_kernel<4,1,false,128> + unit_merge_kernel
+    # (profiles/spec_verify_b64_hbm_counters.md)
+    "spec_verify_b64": 1203410123,
 }
 
 # The same for one pa_cache_append call.

@@ -277,3 +277,29 @@ def test_check_inputs_page_size(dev, P):
     bt[1, :] = 0
     assert flags(bt=bt, ctx=ctx, max_ctx=rows * P) == (pa.CHECK_CONTEXT_BLOCKS |
                                                         pa.CHECK_CONTEXT_BOUND)
+
+
+def test_largest_page_size(dev):
+    """Pages of 1024 slots (64 tiles each): decode on both grids, a short
+    run and query tiles, with contexts inside the first page, across pages
+    and ending one slot into a page."""
+    P = 1024
+    log("[page size 1024]")
+    ctx = [1, 1000, 1025, 3000, 0, 4097]
+    spec = workloads.small_spec("p1024_dec", seed=3950, contexts=ctx, queries=[1] * len(ctx),
+                                page_size=P)
+    b = workloads.generate(spec, dev)
+    for merge in ("separate", "even"):
+        out, lse = run_decode(b, torch.float32, 5, variant=MERGE_VARIANT[merge])
+        compare(b, out, lse, label=f"decode P={P} {merge}")
+    spec = workloads.small_spec("p1024_pre", seed=3951, contexts=[3000, 1025, 40, 4097],
+                                queries=[300, 4, 40, 1], page_size=P, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    for dt in (torch.bfloat16, torch.float32):
+        out, lse = run_prefill(b, dt)
+        compare(b, out, lse, label=f"prefill P={P} {dt}")
+    spec = workloads.small_spec("p1024_sr", seed=3952, contexts=[3000, 1025, 40, 4097],
+                                queries=[4, 3, 4, 2], page_size=P, decode_layout=False)
+    b = workloads.generate(spec, dev)
+    out, lse = run_prefill(b, torch.float32)
+    compare(b, out, lse, label=f"short runs P={P}")
