@@ -49,12 +49,15 @@
  * graph.  Lengths, tables and query_start_loc are read on the device only;
  * the grid depends only on host fields of pa_problem (a static launch grid,
  * [IBM-PA] five-step list, static-grid and graph steps).  The library's
- * only mutable global state is a cache of occupancy figures (compute units
+ * mutable global state is (1) a cache of occupancy figures (compute units
  * x resident workgroups per unit, for the kernels whose grid is sized to
- * the chip), kept per device and keyed on the device of the call's stream;
- * each entry is filled on first use with a relaxed atomic store, and
- * concurrent first calls compute and store the same value.  The tile table
- * is constant.
+ * the chip), kept per device and keyed on the device of the call's stream,
+ * each entry filled on first use with a relaxed atomic store (concurrent
+ * first calls compute and store the same value); and (2) for
+ * pa_decode_noalloc only, a PA_NOALLOC_SCRATCH_BYTES device array that
+ * every GPU holds until the process ends, with its per-device address
+ * cached the same way, and whose contents calls on one GPU share (see that
+ * entry point).  The tile table is constant.
  *
  * Errors: every host-side argument is checked before anything is enqueued;
  * a failed check returns a status and enqueues nothing.  A failed launch
@@ -108,7 +111,7 @@ typedef struct pa_problem {
 
 /* Launch shape chosen by pa_select_tiles (or forced by a tuning sweep). */
 typedef struct pa_tiles {
-  int32_t kv_tile;           /* keys per inner step (16 decode; 32/64 prefill)   */
+  int32_t kv_tile;           /* keys per inner step (16 decode, 32 prefill)      */
   int32_t num_splits;        /* split-KV count S of decode rows (>= 1)           */
   int32_t waves_per_wg;      /* wavefronts per workgroup                         */
   int32_t q_tokens_per_tile; /* query tokens per prefill workgroup               */
@@ -149,8 +152,8 @@ pa_status pa_workspace_size(const pa_problem* problem, const pa_tiles* tiles,
 /* Decode: one query token per sequence (T = num_seqs, row s of q belongs to
  * sequence s; causal has no effect).  Split-KV ([IBM-PA] five-step list,
  * parallel tiled softmax step): with tiles->num_splits = S > 1 the context of
- * each sequence is cut into S contiguous, page-aligned ranges processed by
- * different workgroups; their (normalised output, lse) partials go to the
+ * each sequence is cut into S contiguous ranges of whole 16-key tiles
+ * processed by different workgroups; their (normalised output, lse) partials go to the
  * workspace and are merged by log-sum-exp in the same call.
  * With tiles->variant bit 1 set (the table's choice) a second kernel merges
  * them: the one behind pa_splitkv_reduce, or on the even-work grid a merge
