@@ -3,8 +3,8 @@ oracle: random query-head groups (G = 1..32), head dims (64, 128, 256),
 batch sizes, length mixes (empty sequences, single tokens, short runs,
 chunks on cached prefixes, a few past 32k keys), causal or not, bf16 or fp32 outputs, with or
 without the LSE, pools in the default layout or seen through other strides
-(head-major storage, or padded rows and heads holding NaN), and sometimes a
-forced split count over a NaN-filled workspace.  Each case goes through
+(head-major storage, or padded rows and heads holding NaN), pages of 16 to
+256 slots, and sometimes a forced split count over a NaN-filled workspace.  Each case goes through
 whatever kernels the host picks for it (decode kernels, short-run kernel,
 query tiles with or without decode workgroups, tile splits), so the routing
 is exercised on shapes no hand-written case names.  Long rows are compared
@@ -12,6 +12,7 @@ on a seeded sample of output rows.  The paged append gets the same random
 batches and pool layouts, compared bit for bit.
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -23,7 +24,8 @@ from test_gpu_parity import compare, dev, log, run_decode, run_prefill  # noqa: 
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 200
+# PA_FUZZ_CASES raises the count for a wider one-off sweep
+N_CASES = int(os.environ.get("PA_FUZZ_CASES", "200"))
 MAX_ROWS = 384  # output rows checked per case (sampled beyond this)
 
 
@@ -70,9 +72,11 @@ def draw_case(i):
     layout = str(rng.choice(["default", "default", "head_major", "padded"]))
     with_lse = bool(rng.integers(0, 3) > 0)
     force = int(rng.choice([0, 0, 0, 2, 3, 8]))  # splits (decode) / tile splits (prefill)
+    # drawn last, so the fields above are those of the 16-slot-page cases
+    P = int(rng.choice([16, 16, 16, 32, 64, 256]))
     return dict(G=G, hkv=hkv, D=D, ctx=ctx, ql=ql, causal=causal, out_dtype=out_dtype,
                 decode_layout=decode_layout, layout=layout, with_lse=with_lse, force=force,
-                seed=7100 + i)
+                P=P, seed=7100 + i)
 
 
 def strided_pools(b, layout):
@@ -95,11 +99,11 @@ def test_random_problem(dev, i):
     c = draw_case(i)
     log(f"[fuzz {i}] G={c['G']} Hkv={c['hkv']} D={c['D']} ctx={c['ctx']} q={c['ql']} "
         f"causal={c['causal']} {c['out_dtype']} decode_layout={c['decode_layout']} "
-        f"layout={c['layout']} lse={c['with_lse']} force={c['force']}")
+        f"layout={c['layout']} lse={c['with_lse']} force={c['force']} P={c['P']}")
     spec = workloads.small_spec(f"fuzz{i}", c["seed"], c["ctx"], c["ql"],
                                 num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"],
                                 head_dim=c["D"], causal=c["causal"],
-                                decode_layout=c["decode_layout"])
+                                decode_layout=c["decode_layout"], page_size=c["P"])
     b = workloads.generate(spec, dev)
     bg = b  # what the GPU sees; the oracle reads b's default layout
     if c["layout"] != "default":
