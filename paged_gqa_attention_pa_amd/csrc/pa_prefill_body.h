@@ -438,7 +438,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
   };
 
   // The run [j0, j0 + nkv) in windows of at most kWinTiles key tiles (one
-  // LDS page-id window each).  Each step j is two phases, each ending in a
+  // LDS window of block offsets each).  Each step j is two phases, each ending in a
   // workgroup barrier:
   //   M(j): S^T of tile j+1 and P.V of tile j-1 (sixteen MFMAs);
   //   V(j): softmax of tile j, store of tile j+3 (loaded during V(j-1)),

@@ -49,7 +49,7 @@ def draw_case(i):
             q = 0
         else:
             q = int(rng.integers(17, 200))
-        # rarely past 32k keys, where the page-id window in LDS is restaged
+        # rarely past 32k keys, where the LDS window of block offsets is restaged
         prefix = 0 if q == 0 else int(rng.choice([0, rng.integers(0, 600), rng.integers(0, 3000),
                                                   rng.integers(0, 3000),
                                                   rng.integers(0, 3000) + 33000 * (i % 7 == 0)]))

@@ -131,7 +131,8 @@ PREFILL_D256 = [
     ("g8", [200, 90], [70, 90], True, 32, 4),
     ("g16", [200, 90], [70, 90], True, 16, 1),
     ("g32", [300, 77], [40, 9], True, 32, 1),
-    # more than 1024 pages: the page-id window (16k keys at 256) is restaged
+    # more than 1024 16-key blocks: the LDS window of block offsets (16k keys
+    # at head dim 256) is restaged
     ("long_context", [20000, 300], [32, 20], True, 32, 8),
 ]
 

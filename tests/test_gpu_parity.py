@@ -295,7 +295,8 @@ PREFILL_CASES = [
     ("decode_rows_first", [900, 40, 260, 513], [1, 1, 100, 200], True),
     ("decode_rows_last", [260, 513, 900, 40], [100, 200, 1, 1], True),
     ("degenerate", [0, 1, 5, 16], [0, 1, 5, 1], True),
-    # more than 2048 pages: the page-id window in LDS is restaged mid-sequence
+    # more than 2048 16-key blocks: the LDS window of block offsets is
+    # restaged mid-sequence
     ("long_context", [40000, 300], [32, 20], True),
     ("long_noncausal", [34000], [40], False),
 ]
