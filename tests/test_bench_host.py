@@ -66,3 +66,40 @@ def test_roofline_bound_follows_the_larger_ideal_time():
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["traffic"] == 123
     ideal = 275e9 / (bench.MFMA_BF16_PEAK_TFS * 1e12)
     assert abs(r["frac"] - round(ideal / (ms * 1e-3), 4)) < 1e-9
+
+
+PROFILES = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+
+
+def _profile_numbers(name):
+    """(algorithmic bytes, traffic bytes) a counter summary states for a line."""
+    import re
+    text = open(os.path.join(PROFILES, f"{name}_hbm_counters.md")).read()
+    m = re.search(r"`bench.py` reports ([0-9,]+) as", text)
+    a = re.search(r"\): ([0-9,]+) → traffic / algorithmic", text)
+    assert m and a, name
+    return int(a.group(1).replace(",", "")), int(m.group(1).replace(",", ""))
+
+
+@pytest.mark.parametrize("table,name", [
+    ("TRAFFIC", "decode_ctx32k"), ("TRAFFIC", "decode_ctx512"), ("TRAFFIC", "decode_b64"),
+    ("TRAFFIC", "decode_b256_ctx8k"), ("PREFILL_TRAFFIC", "prefill_chunk2048"),
+    ("PREFILL_TRAFFIC", "mixed_unified"), ("PREFILL_TRAFFIC", "spec_verify_b64")])
+def test_traffic_constants_match_their_profiles(table, name):
+    """Each roofline.traffic constant is the number its committed counter
+    summary says the bench reports, and lies between the algorithmic bytes
+    and 1.35 times them (more would mean re-reads worth fixing, less a
+    mistyped constant)."""
+    alg, reported = _profile_numbers(name)
+    value = getattr(bench, table)[name]
+    assert value == reported
+    assert alg <= value <= 1.35 * alg
+
+
+def test_append_traffic_constant_matches_its_profile():
+    import re
+    text = open(os.path.join(PROFILES, "append_prefill_chunk2048_hbm_counters.md")).read()
+    reported = int(re.search(r"`bench.py` reports ([0-9,]+) as", text).group(1).replace(",", ""))
+    assert bench.APPEND_TRAFFIC["prefill_chunk2048"] == reported
+    alg = 8192 * 8 * 2 * 128 * 2 * 2  # tokens x kv heads x (K, V) x D x bf16, read + written
+    assert alg <= reported <= 1.05 * alg
