@@ -28,9 +28,12 @@
 //
 // Split-KV (the parallel tiled softmax step of the same list): a sequence
 // with n_act > 1 non-empty splits writes normalised partials (O_k, lse_k) to
-// the workspace; the last of its workgroups to finish (an agent-scope atomic
-// counter per (sequence, kv head), released and acquired with device fences)
-// merges them by log-sum-exp and resets the counter to zero.  A sequence
+// the workspace, merged by log-sum-exp either in a second launch
+// (splitkv_reduce_kernel / unit_merge_kernel, the default) or, with FUSED,
+// by the last of its workgroups to finish (an agent-scope atomic counter per
+// (sequence, kv head), released and acquired with device fences, reset to
+// zero by the merging workgroup).  On gfx950 each agent-scope release writes
+// back the XCD's L2, which costs more than the second launch.  A sequence
 // with one non-empty split writes its output directly.
 #pragma once
 

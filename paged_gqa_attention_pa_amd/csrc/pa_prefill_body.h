@@ -198,9 +198,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int id, int
       qb[ks] = row_valid ? as_bf16x8(ld16(qrow + 16 * ks)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
-  // LDS, three buffers each of K and V, both row-major [key][dim] (padded
-  // rows).  While tile j is being finished (softmax, P.V), the S^T MFMAs of
-  // tile j+1 already run and tile j+2 is being stored: one barrier per tile.
+  // LDS: kKBufs K tiles and kVBufs V tiles, both row-major [key][dim]
+  // (padded rows); the step loop below says which tile each buffer holds
+  // when.
   auto k_lds = reinterpret_cast<uint16_t(*)[kKvTile * kLdsStride]>(smem);
   auto v_lds =
       reinterpret_cast<uint16_t(*)[kKvTile * kVStride]>(smem + kKBufs * kKvTile * kLdsStride * 2);
