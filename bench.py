@@ -120,6 +120,19 @@ def prefill_flops(b):
     return 4 * D * Hq * total
 
 
+def spread(per_ms):
+    """p10 / median / p90 of the time per step over the timed steps, in us
+    (a step's time is the average over the graph replay that holds it)."""
+    xs = sorted(per_ms)
+    if not xs:
+        return None
+
+    def q(f):
+        return round(xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))] * 1e3, 2)
+
+    return {"p10_us": q(0.1), "p50_us": q(0.5), "p90_us": q(0.9), "steps": len(xs)}
+
+
 def whole_replays(steps, per):
     """Secondary lines time a whole number of multi-step replays: a replay of
     a single step costs 5-10 us more on this stack (see --launch-study)."""
@@ -204,6 +217,7 @@ def decode_line(torch, pa, workloads, args, dev):
     gbs = dd["nbytes"] / (ms * 1e-3) / 1e9
     return {"workload": args.workload, "metric": "decode KV GB/s (4096 B per context token)",
             "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(ms * 1e3, 2),
+            "step_us": spread(dd["per"]),
             "bytes_per_step": dd["nbytes"], "pool_copies": args.pools,
             "rotated_mib": round(dd["pool_bytes"] / 2 ** 20, 1),
             "tiles": dd["tiles"].as_dict(),
@@ -287,7 +301,7 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
             "metric": "attention TFLOP/s over causal pairs (4*D flop each) and GB/s of "
                       "K/V + Q + O bytes",
             "value": round(tfs, 2), "unit": "TFLOP/s", "us_per_step": round(avg_ms * 1e3, 2),
-            "ms_per_step": round(avg_ms, 4), "gb_per_s": round(gbs, 1),
+            "ms_per_step": round(avg_ms, 4), "step_us": spread(per), "gb_per_s": round(gbs, 1),
             "flops_per_step": flops, "bytes_per_step": nbytes,
             "input_copies": len(sets),
             "rotated_mib": round(len(sets) * set_bytes / 2 ** 20, 1),
@@ -342,7 +356,7 @@ def bench_append(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk20
                         f"heads (K and V) into their pages",
             "metric": "paged KV append GB/s (new rows read + written)",
             "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(avg_ms * 1e3, 2),
-            "bytes_per_step": nbytes,
+            "step_us": spread(per), "bytes_per_step": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": APPEND_TRAFFIC.get(name)}}
@@ -486,6 +500,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_us": spread(d["per"]),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -103,3 +103,12 @@ def test_append_traffic_constant_matches_its_profile():
     assert bench.APPEND_TRAFFIC["prefill_chunk2048"] == reported
     alg = 8192 * 8 * 2 * 128 * 2 * 2  # tokens x kv heads x (K, V) x D x bf16, read + written
     assert alg <= reported <= 1.05 * alg
+
+
+def test_step_spread_quantiles():
+    """p10 / median / p90 over per-step times (ms in, us out), by rank."""
+    per = [0.001 * (i + 1) for i in range(11)]  # 1..11 us, shuffled below
+    got = bench.spread(per[5:] + per[:5])
+    assert got == {"p10_us": 2.0, "p50_us": 6.0, "p90_us": 10.0, "steps": 11}
+    assert bench.spread([0.0357] * 60)["p50_us"] == 35.7
+    assert bench.spread([]) is None
