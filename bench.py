@@ -425,6 +425,31 @@ def calibrate_copy(torch, dev, mib):
     note(f"calibration: 4 copies of {mib} MiB")
 
 
+def measured_copy_peak(torch, dev, mib=1024, reps=10):
+    """HBM rate of a plain device-to-device copy (torch) of `mib` MiB, bytes
+    read + written: the practical streaming rate of this machine, reported as
+    context beside the spec peak."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kind": f"device-to-device copy of {mib} MiB (torch), read + written bytes",
+            "gb_per_s": round(gbs, 1), "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(workloads, b, seconds):
     """The fp64 oracle on the same decode workload, on the host cores."""
     import oracle
@@ -572,6 +597,11 @@ def main():
         others["append_decode_b64"] = app
         note(f"append decode_b64: {app['us_per_step']} us")
         result["others"] = others
+    mp = measured_copy_peak(torch, dev)
+    result["measured_peak"] = mp
+    result["roofline"]["frac_of_measured"] = round(result["roofline"]["achieved"] /
+                                                   mp["gb_per_s"], 4)
+    note(f"measured copy rate: {mp['gb_per_s']} GB/s")
     if not args.no_cpu_baseline:
         spec = workloads.WORKLOADS[args.workload]
         result["cpu_baseline"] = cpu_baseline(workloads, workloads.generate(spec, dev, "zero"),
