@@ -456,12 +456,16 @@ def test_prefill_page_permutation_and_nan_bitexact(dev):
 
 # ---------------------------------------------------------------- reduce ----
 
-@pytest.mark.parametrize("S", [1, 2, 7, 64, 256])
-def test_reduce_random_partials(dev, S):
-    log(f"[reduce S={S}]")
+@pytest.mark.parametrize("S,D", [(1, 128), (2, 128), (7, 128), (64, 128), (256, 128),
+                                 (1000, 64), (4096, 128), (33, 256), (3, 1024), (17, 12),
+                                 (5, 4)])
+def test_reduce_random_partials(dev, S, D):
+    """pa_splitkv_reduce alone over its whole argument range: 1 to 4096
+    splits, head dims from 4 to 1024 (any multiple of 4)."""
+    log(f"[reduce S={S} D={D}]")
     g = torch.Generator(device="cpu")
-    g.manual_seed(500 + S)
-    rows, D = 37, 128
+    g.manual_seed(500 + S + D)
+    rows = 37
     po = torch.randn((rows, S, D), generator=g, dtype=torch.float32)
     pl = torch.randn((rows, S), generator=g, dtype=torch.float32) * 20
     drop = torch.rand((rows, S), generator=g) < 0.3
