@@ -333,3 +333,35 @@ def test_status_strings(lib):
     for s in range(5):
         assert pa.status_string(s)
     assert "workspace" in pa.status_string(pa.PA_ERR_WORKSPACE)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without a built libpa.so every entry point raises: there is no
+    fallback path that would compute anything elsewhere."""
+    import torch
+    monkeypatch.setattr(pa, "_lib", None)
+    monkeypatch.setattr(pa, "_LIB_PATH", str(tmp_path / "libpa.so"))
+    with pytest.raises(ImportError):
+        pa.load()
+    t = torch.zeros((1, 32, 128), dtype=torch.bfloat16)
+    pool = torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    ctx = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ImportError):
+        pa.decode(t, pool, pool, bt, ctx, 0.088, 16)
+    with pytest.raises(ImportError):
+        pa.prefill(t, torch.tensor([0, 1], dtype=torch.int32), pool, pool, bt, ctx, 0.088, 16, 1)
+
+
+def test_product_code_never_imports_the_oracle():
+    """Only the tests, the smoke check and the benchmark's CPU baseline may
+    reach the oracle; the package (binding, build, tuning) must not."""
+    pkg = os.path.join(ROOT, "paged_gqa_attention_pa_amd")
+    offenders = []
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                if re.search(r"^\s*(import|from)\s+oracle\b|pa_oracle|liboracle", text, re.M):
+                    offenders.append(os.path.join(dirpath, f))
+    assert not offenders, offenders
