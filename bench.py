@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="force num_splits (0 = table)")
     ap.add_argument("--waves", type=int, default=0, help="force waves per workgroup (0 = table)")
     ap.add_argument("--variant", type=int, default=-1, help="force pa_tiles.variant (-1 = table)")
+    ap.add_argument("--layout", default="head_major", choices=("head_major", "token_major"),
+                    help="storage order of the K/V pools' pages (same values, other strides); "
+                         "the run also times the headline workload in the other order")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-workload", default="prefill_chunk2048",
                     help="workload of --prefill-only (prefill_chunk2048 or mixed_unified)")
@@ -167,8 +170,8 @@ def bench_decode(torch, pa, workloads, args, dev):
     spec = workloads.WORKLOADS[args.workload]
     if not spec.decode_layout:
         raise SystemExit(f"{args.workload} is not a decode workload")
-    b = workloads.generate(spec, dev, fill="zero")
-    note(f"generated {spec.name}: B={b.num_seqs} max_ctx={b.max_context_len}")
+    b = workloads.with_layout(workloads.generate(spec, dev, fill="zero"), args.layout)
+    note(f"generated {spec.name}: B={b.num_seqs} max_ctx={b.max_context_len} ({args.layout})")
     pools = [(b.k_pool, b.v_pool)]
     for _ in range(max(1, args.pools) - 1):
         pools.append((b.k_pool.clone(), b.v_pool.clone()))
@@ -217,7 +220,7 @@ def decode_line(torch, pa, workloads, args, dev):
     gbs = dd["nbytes"] / (ms * 1e-3) / 1e9
     return {"workload": args.workload, "metric": "decode KV GB/s (4096 B per context token)",
             "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(ms * 1e3, 2),
-            "step_us": spread(dd["per"]),
+            "step_us": spread(dd["per"]), "kv_layout": args.layout,
             "bytes_per_step": dd["nbytes"], "pool_copies": args.pools,
             "rotated_mib": round(dd["pool_bytes"] / 2 ** 20, 1),
             "tiles": dd["tiles"].as_dict(),
@@ -253,13 +256,13 @@ def roofline(nbytes, flops, ms, traffic):
 
 
 def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2048",
-                  copies=3):
+                  copies=3, layout="head_major"):
     """One pa_prefill call per step, four steps per graph replay.  Each step
     reads a different copy of Q and of the pools and writes a different
     output (`copies` of them, together larger than the 256 MiB Infinity
     Cache), so no step finds its inputs in that cache."""
     spec = workloads.WORKLOADS[name]
-    b = workloads.generate(spec, dev, fill="zero")
+    b = workloads.with_layout(workloads.generate(spec, dev, fill="zero"), layout)
     max_ctx, max_q = b.max_context_len, b.max_query_len
     problem = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
                               max_ctx, max_q, causal=spec.causal)
@@ -301,7 +304,8 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
             "metric": "attention TFLOP/s over causal pairs (4*D flop each) and GB/s of "
                       "K/V + Q + O bytes",
             "value": round(tfs, 2), "unit": "TFLOP/s", "us_per_step": round(avg_ms * 1e3, 2),
-            "ms_per_step": round(avg_ms, 4), "step_us": spread(per), "gb_per_s": round(gbs, 1),
+            "ms_per_step": round(avg_ms, 4), "step_us": spread(per), "kv_layout": layout,
+            "gb_per_s": round(gbs, 1),
             "flops_per_step": flops, "bytes_per_step": nbytes,
             "input_copies": len(sets),
             "rotated_mib": round(len(sets) * set_bytes / 2 ** 20, 1),
@@ -315,14 +319,14 @@ def append_bytes(b):
 
 
 def bench_append(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2048",
-                 copies=8, pool_copies=8):
+                 copies=8, pool_copies=8, layout="head_major"):
     """pa_cache_append of a batch's new tokens, eight steps per graph replay.
     Each step appends a different copy of the new rows, into a different copy
     of the pools when pool_copies = copies (copies of both together exceed the
     256 MiB Infinity Cache for the chunked prefill), so the rows stream from
     HBM and the written pages leave for HBM."""
     spec = workloads.WORKLOADS[name]
-    b = workloads.generate(spec, dev, fill="zero")
+    b = workloads.with_layout(workloads.generate(spec, dev, fill="zero"), layout)
     sets = []
     for i in range(copies):
         kn, vn = workloads.new_kv(b, seed=500 + i)
@@ -356,7 +360,7 @@ def bench_append(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk20
                         f"heads (K and V) into their pages",
             "metric": "paged KV append GB/s (new rows read + written)",
             "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(avg_ms * 1e3, 2),
-            "step_us": spread(per), "bytes_per_step": nbytes,
+            "step_us": spread(per), "kv_layout": layout, "bytes_per_step": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": APPEND_TRAFFIC.get(name)}}
@@ -460,7 +464,7 @@ def cpu_baseline(workloads, b, seconds):
         v_pool=workloads.bf16_bits(b.v_pool), block_tables=b.block_tables.cpu().numpy(),
         context_lens=b.context_lens.cpu().numpy(), query_start_loc=qsl,
         num_kv_heads=b.spec.num_kv_heads, page_size=b.spec.page_size,
-        strides=b.kv_strides(), scale=b.spec.scale, causal=b.spec.causal)
+        strides=b.host_strides(), scale=b.spec.scale, causal=b.spec.causal)
     threads = oracle.default_threads()
     runs, t0 = 0, time.perf_counter()
     while True:
@@ -497,14 +501,14 @@ def main():
         return
     if args.append_only:
         app = bench_append(torch, pa, workloads, dev, args.steps, args.warmup,
-                           name=args.prefill_workload)
+                           name=args.prefill_workload, layout=args.layout)
         note(f"append: {app['us_per_step']} us, {app['value']} GB/s")
         calibrate_copy(torch, dev, args.calibrate_copy)
         print(json.dumps(app), flush=True)
         return
     if args.prefill_only:
         pre = bench_prefill(torch, pa, workloads, dev, args.steps, args.warmup,
-                            name=args.prefill_workload)
+                            name=args.prefill_workload, layout=args.layout)
         note(f"prefill: {pre['value']} TFLOP/s")
         calibrate_copy(torch, dev, args.calibrate_copy)
         print(json.dumps(pre), flush=True)
@@ -541,6 +545,7 @@ def main():
             "pool_copies": args.pools,
             "kv_bytes_per_step": d["nbytes"],
             "graph": "hipGraph replays, one decode step per pool copy in each",
+            "kv_layout": args.layout,
         },
         "roofline": {
             "bound": "hbm",
@@ -555,6 +560,14 @@ def main():
     del d, b
     torch.cuda.empty_cache()
     if not args.no_prefill:
+        # the same headline workload with the pools' pages in the other
+        # storage order (same values, same kernels and launch shape)
+        other = "token_major" if args.layout == "head_major" else "head_major"
+        sub = argparse.Namespace(**{**vars(args), "layout": other})
+        result["other_layout"] = decode_line(torch, pa, workloads, sub, dev)
+        note(f"{args.workload} ({other}): {result['other_layout']['us_per_step']} us, "
+             f"{result['other_layout']['value']} GB/s")
+        torch.cuda.empty_cache()
         # Every config of the five-config set, each with its own roofline.
         # Pool copies per decode step: enough that the copies cycled exceed
         # the 256 MiB Infinity Cache (64 pages x 2 pools x 32 KiB = 4 MiB per
@@ -572,14 +585,15 @@ def main():
             torch.cuda.empty_cache()
         for name, copies in (("prefill_chunk2048", 3), ("mixed_unified", 2)):
             configs[name] = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
-                                          max(8, args.warmup), name=name, copies=copies)
+                                          max(8, args.warmup), name=name, copies=copies,
+                                          layout=args.layout)
             c = configs[name]
             note(f"{name}: {c['us_per_step']} us, {c['value']} TFLOP/s, {c['gb_per_s']} GB/s, "
                  f"roofline {c['roofline']['bound']} {c['roofline']['frac']}")
             torch.cuda.empty_cache()
         result["configs"] = configs
         result["append"] = bench_append(torch, pa, workloads, dev, max(16, args.steps // 2),
-                                        max(8, args.warmup))
+                                        max(8, args.warmup), layout=args.layout)
         note(f"append: {result['append']['us_per_step']} us, {result['append']['value']} GB/s")
     if args.all:
         others = {}
@@ -589,11 +603,13 @@ def main():
         note(f"decode_b256_ctx8k: {others['decode_b256_ctx8k']}")
         torch.cuda.empty_cache()
         spec_v = bench_prefill(torch, pa, workloads, dev, max(8, args.steps // 2),
-                               max(8, args.warmup), name="spec_verify_b64", copies=2)
+                               max(8, args.warmup), name="spec_verify_b64", copies=2,
+                               layout=args.layout)
         others["spec_verify_b64"] = spec_v
         note(f"spec_verify_b64: {spec_v['us_per_step']} us, {spec_v['gb_per_s']} GB/s")
         app = bench_append(torch, pa, workloads, dev, max(16, args.steps // 2),
-                           max(8, args.warmup), name="decode_b64", pool_copies=1)
+                           max(8, args.warmup), name="decode_b64", pool_copies=1,
+                           layout=args.layout)
         others["append_decode_b64"] = app
         note(f"append decode_b64: {app['us_per_step']} us")
         result["others"] = others

@@ -133,6 +133,13 @@ class Batch:
         s = self.k_pool.stride()
         return int(s[0]), int(s[1]), int(s[2])
 
+    def host_strides(self):
+        """(page, token, head) strides of the pools' host copies (bf16_bits
+        copies them in logical [page, slot, head, dim] order, contiguous),
+        whatever order the device pools store their pages in."""
+        _, P, Hkv, D = self.k_pool.shape
+        return P * Hkv * D, Hkv * D, D
+
 
 def _lengths(spec: WorkloadSpec, g: torch.Generator):
     ctx, ql = [], []
@@ -233,6 +240,28 @@ def generate(spec: WorkloadSpec, device="cpu", fill: str = "nan") -> Batch:
     return Batch(spec=spec, q=q, k_pool=k_pool, v_pool=v_pool, block_tables=bt,
                  context_lens=torch.tensor(ctx, dtype=torch.int32, device=device),
                  query_start_loc=qsl, query_lens=ql, used_pages=used)
+
+
+# How the pools store a page: token_major keeps the generated order
+# [page][slot][kv head][dim] (one token's heads side by side); head_major
+# stores [page][kv head][slot][dim] (one head's slots side by side, so a 16-key
+# tile of a head is one contiguous 4 KiB run at D = 128).  Both are seen
+# through the same logical [page, slot, head, dim] tensor, with other strides.
+KV_LAYOUTS = ("token_major", "head_major")
+
+
+def with_layout(batch: Batch, layout: str) -> Batch:
+    """The batch with its pools stored in `layout` (same values)."""
+    if layout == "token_major":
+        return batch
+    if layout != "head_major":
+        raise ValueError(f"layout must be one of {KV_LAYOUTS}")
+
+    def head_major(t):
+        return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+    return dataclasses.replace(batch, k_pool=head_major(batch.k_pool),
+                               v_pool=head_major(batch.v_pool))
 
 
 def new_kv(batch: Batch, seed: int):

@@ -31,7 +31,7 @@ def batch_to_oracle(batch: workloads.Batch) -> oracle.PagedInputs:
         block_tables=batch.block_tables.cpu().numpy(),
         context_lens=batch.context_lens.cpu().numpy(), query_start_loc=qsl,
         num_kv_heads=batch.spec.num_kv_heads, page_size=batch.spec.page_size,
-        strides=batch.kv_strides(), scale=batch.spec.scale, causal=batch.spec.causal)
+        strides=batch.host_strides(), scale=batch.spec.scale, causal=batch.spec.causal)
 
 
 class DenseProblem:

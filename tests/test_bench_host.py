@@ -112,3 +112,13 @@ def test_step_spread_quantiles():
     assert got == {"p10_us": 2.0, "p50_us": 6.0, "p90_us": 10.0, "steps": 11}
     assert bench.spread([0.0357] * 60)["p50_us"] == 35.7
     assert bench.spread([]) is None
+
+
+def test_bench_layout_default_and_choices(monkeypatch):
+    """The benchmark stores the pools' pages head-major unless told
+    otherwise, and accepts only the layouts the workloads know."""
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    assert bench.parse().layout == "head_major"
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--layout", "token_major"])
+    assert bench.parse().layout == "token_major"
+    assert set(workloads.KV_LAYOUTS) == {"head_major", "token_major"}

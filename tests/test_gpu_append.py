@@ -168,14 +168,14 @@ def _oracle_attention_after_append(b, kn, vn, k_bits, v_bits, rows=None):
     """Oracle append on host copies of the pre-append pools, then oracle
     attention over the result."""
     qsl = None if b.query_start_loc is None else b.query_start_loc.cpu().numpy()
-    kp, vp = oracle.append(k_bits, v_bits, b.spec.page_size, b.kv_strides(), _bits(kn),
+    kp, vp = oracle.append(k_bits, v_bits, b.spec.page_size, b.host_strides(), _bits(kn),
                            _bits(vn), b.block_tables.cpu().numpy(),
                            b.context_lens.cpu().numpy(), qsl)
     inp = oracle.PagedInputs(q=_bits(b.q), k_pool=kp, v_pool=vp,
                              block_tables=b.block_tables.cpu().numpy(),
                              context_lens=b.context_lens.cpu().numpy(), query_start_loc=qsl,
                              num_kv_heads=b.spec.num_kv_heads, page_size=b.spec.page_size,
-                             strides=b.kv_strides(), scale=b.spec.scale, causal=b.spec.causal)
+                             strides=b.host_strides(), scale=b.spec.scale, causal=b.spec.causal)
     return oracle.attention(inp, rows=rows)
 
 

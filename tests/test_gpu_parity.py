@@ -502,17 +502,19 @@ def _sample_rows(b, n, seed):
     return np.array(sorted(rows), dtype=np.int64)
 
 
+@pytest.mark.parametrize("layout", workloads.KV_LAYOUTS)
 @pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER + ["decode_b256_ctx8k"])
-def test_named_workload(dev, name):
+def test_named_workload(dev, name, layout):
     """Each workload at full size, launched as the benchmark launches it
     (table launch shape, bf16 output, no LSE: for the query-tile and
-    short-run kernels that is the variant with P rounded to bf16), every
-    row compared with the oracle except at batch 256 (a seeded sample);
-    query-layout workloads are also run with an LSE (the precise variant) on
-    sampled rows."""
-    log(f"[workload {name}]")
+    short-run kernels that is the variant with P rounded to bf16), with the
+    pools' pages stored in either order (the benchmark stores them head
+    major), every row compared with the oracle except at batch 256 (a
+    seeded sample); query-layout workloads are also run with an LSE (the
+    precise variant) on sampled rows."""
+    log(f"[workload {name} {layout}]")
     spec = workloads.WORKLOADS[name]
-    b = workloads.generate(spec, dev, fill="nan")
+    b = workloads.with_layout(workloads.generate(spec, dev, fill="nan"), layout)
     if spec.decode_layout:
         out, _ = run_decode(b, torch.bfloat16, with_lse=False)
         rows = None

@@ -43,7 +43,7 @@ def _randn_bf16(g, shape, dev):
 
 
 def _mirror_append(b, host, kn, vn, ctx, qsl):
-    host[0], host[1] = oracle.append(host[0], host[1], b.spec.page_size, b.kv_strides(),
+    host[0], host[1] = oracle.append(host[0], host[1], b.spec.page_size, b.host_strides(),
                                      workloads.bf16_bits(kn), workloads.bf16_bits(vn),
                                      b.block_tables.cpu().numpy(), np.asarray(ctx, np.int32),
                                      None if qsl is None else np.asarray(qsl, np.int32))
@@ -55,7 +55,7 @@ def _check(b, host, q, ctx, qsl, out, label):
                              context_lens=np.asarray(ctx, np.int32),
                              query_start_loc=None if qsl is None else np.asarray(qsl, np.int32),
                              num_kv_heads=HKV, page_size=b.spec.page_size,
-                             strides=b.kv_strides(), scale=b.spec.scale, causal=True)
+                             strides=b.host_strides(), scale=b.spec.scale, causal=True)
     ref, _ = oracle.attention(inp)
     got = out.float().cpu().numpy().reshape(ref.shape)
     diff = np.abs(got - ref)

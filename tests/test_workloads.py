@@ -80,3 +80,36 @@ def test_named_workload_plans(name):
     if name == "mixed_unified":
         assert len(ctx) == 18 and ql[:16] == [1] * 16 and ql[16:] == [512, 512]
         assert min(ctx[:16]) >= 512 and max(ctx[:16]) <= 16384 and ctx[16:] == [4608, 4608]
+
+
+def test_head_major_layout_keeps_values():
+    """with_layout stores each page head by head without changing a value:
+    the logical pools are equal, the strides are head-major, and the oracle
+    gives the same bits from the storage of either layout read with its own
+    strides."""
+    import oracle
+    spec = workloads.small_spec("hm", seed=21, contexts=[40, 17, 1], queries=[5, 17, 1],
+                                num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                decode_layout=False)
+    b = workloads.generate(spec, "cpu")
+    h = workloads.with_layout(b, "head_major")
+    assert workloads.with_layout(b, "token_major") is b
+    assert torch.equal(h.k_pool.view(torch.int16), b.k_pool.view(torch.int16))
+    assert torch.equal(h.v_pool.view(torch.int16), b.v_pool.view(torch.int16))
+    npg, P, Hkv, D = b.k_pool.shape
+    assert h.kv_strides() == (P * Hkv * D, D, P * D)
+    assert h.host_strides() == b.host_strides() == (P * Hkv * D, Hkv * D, D)
+    outs = []
+    for bb in (b, h):
+        # the storage itself, as the device kernels read it
+        store = lambda t: t.permute(0, 2, 1, 3).contiguous() if bb is h else t  # noqa: E731
+        inp = oracle.PagedInputs(
+            q=workloads.bf16_bits(bb.q), k_pool=workloads.bf16_bits(store(bb.k_pool)),
+            v_pool=workloads.bf16_bits(store(bb.v_pool)),
+            block_tables=bb.block_tables.numpy(), context_lens=bb.context_lens.numpy(),
+            query_start_loc=bb.query_start_loc.numpy(), num_kv_heads=Hkv, page_size=P,
+            strides=bb.kv_strides(), scale=spec.scale, causal=True)
+        outs.append(oracle.attention(inp))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    with pytest.raises(ValueError):
+        workloads.with_layout(b, "slot_major")
