@@ -37,37 +37,38 @@ DECODE_BYTES_PER_TOKEN = 4096
 
 # HBM bytes per call from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (each
 # scaled by what it reads for a plain 256 MiB device copy), for the kernels
-# and launch shapes as last profiled; None where they changed since.
+# and launch shapes as last profiled, on head-major pools (the default
+# --layout); None where they changed since.
 TRAFFIC = {
     # decode_kernel<4,4,false> + splitkv_reduce_kernel, 32 splits
     # (profiles/decode_ctx32k_hbm_counters.md)
-    "decode_ctx32k": 135727485,
+    "decode_ctx32k": 135727556,
     # decode_kernel<4,4,false> + splitkv_reduce_kernel, 8 splits
     # (profiles/decode_ctx512_hbm_counters.md)
-    "decode_ctx512": 2691226,
+    "decode_ctx512": 2691108,
     # decode_even_kernel<4,4> + unit_merge_kernel, split bound 4
     # (profiles/decode_b64_hbm_counters.md)
-    "decode_b64": 1141207279,
+    "decode_b64": 1141282078,
     # decode_even_kernel<4,8> + unit_merge_kernel, split bound 128
     # (profiles/decode_b256_ctx8k_hbm_counters.md)
-    "decode_b256_ctx8k": 8598464767,
+    "decode_b256_ctx8k": 8598634829,
 }
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {
     # unified_kernel<4,false,128> (profiles/prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 184974034,
+    "prefill_chunk2048": 184975394,
     # unified_kernel<4,false,128> + splitkv_reduce_kernel
     # (profiles/mixed_unified_hbm_counters.md)
-    "mixed_unified": 643195419,
+    "mixed_unified": 643197832,
     # verify_kernel<4,1,false,128> + unit_merge_kernel
     # (profiles/spec_verify_b64_hbm_counters.md)
-    "spec_verify_b64": 1203410123,
+    "spec_verify_b64": 1203498318,
 }
 
 # The same for one pa_cache_append call.
 APPEND_TRAFFIC = {
     # append_kernel (profiles/append_prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 67206941,
+    "prefill_chunk2048": 67198731,
 }
 
 
