@@ -26,7 +26,11 @@
  *   k_pool/v_pool element (page, slot, kv_head, d) sits at
  *                 page*kv_stride_page + slot*kv_stride_token
  *                 + kv_head*kv_stride_head + d   (d stride is 1)
- *                 K and V share the strides.  Default: [pages, P, Hkv, D].
+ *                 K and V share the strides.  Token-major storage is
+ *                 [pages, P, Hkv, D]; head-major storage [pages, Hkv, P, D]
+ *                 (kv_stride_head = P*D, kv_stride_token = D) keeps a head's
+ *                 slots of a page in one run, which the decode kernels
+ *                 stream faster on gfx950 (same results, bit for bit).
  *                 Each stride, and P * kv_stride_token, must be below 2^31
  *                 elements, and max_blocks_per_seq * P / 16 below 2^31
  *                 (PA_ERR_UNSUPPORTED otherwise).
