@@ -55,17 +55,19 @@ constexpr int rows_of() {
   return 32 * waves_of<D>();
 }
 // K and V LDS rows (bf16 elements) for head dim D: K rows padded by 8
-// (272 B at D = 128), V rows by 48 (352 B at 128: the four rows of a
-// transposing read group fall on disjoint banks); at 256, V rows are padded
-// by 16 (544 B: rows 8 banks apart, again disjoint over a group's four rows)
-// so that the ring fits in LDS.
+// (272 B at D = 128: the 16-byte row reads of sixteen lanes cover all 64
+// banks once); V rows padded by 32 (320 B at 128, 192 B at 64: consecutive
+// rows start 16 banks apart, so the four rows a transposing read group
+// touches, and the four more of the other group of the same 32 lanes, fall
+// on disjoint banks); at 256, V rows are padded by 16 (544 B: rows 8 banks
+// apart, disjoint over a group's four rows) so that the ring fits in LDS.
 template <int D>
 constexpr int k_stride() {
   return D + 8;
 }
 template <int D>
 constexpr int v_stride() {
-  return D == 256 ? D + 16 : D + 48;
+  return D == 256 ? D + 16 : D + 32;
 }
 constexpr int kKBufs = 4;                 // LDS K tile buffers
 constexpr int kVBufs = 5;                 // LDS V tile buffers (V is read one step later)
