@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/pa.h"
 #include "pa_internal.h"
 #include "pa_tile_table.h"
@@ -172,6 +174,35 @@ pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; 
 bool may_hold_decode_rows(const pa_problem* pb) {
   return pb->max_query_len <= 1 ||
          (int64_t)pb->total_query_tokens < (int64_t)pb->num_seqs * pb->max_query_len;
+}
+
+// In a unified launch, do the single-token sequences run as split decode
+// workgroups beside the query tiles?  Only at head dim 128 and G <= 8 (the
+// decode body's shapes); elsewhere each one is a query tile of its own.
+bool decode_rows_apart(const pa_problem* pb) {
+  const int G = pb->num_q_heads / pb->num_kv_heads;
+  return may_hold_decode_rows(pb) && G <= 8 && pb->head_dim == kHeadDim;
+}
+
+// Key-run splits of the query tiles of a batch whose single-token sequences
+// run as query tiles.  Such a tile holds one token yet walks the whole
+// context at the cost of a full tile, so the longest one sets the launch
+// time unless its keys are split.  Measured on gfx950 (16 single-token
+// sequences with contexts up to 16k beside two 512-token chunks): the best
+// runs hold about 32 * head_dim keys (D = 64: 8 splits, 370 -> 245 us;
+// G = 16 at D = 128: 4 splits, 536 -> 336 us; D = 256: 2 splits,
+// 802 -> 560 us), and splitting further than about eight workgroups per CU
+// (2048 in all) only adds partial traffic.
+int mixed_tile_splits(const pa_problem* pb) {
+  const int qt = query_tile_tokens(pb);
+  const int64_t tiles = ((int64_t)pb->total_query_tokens + qt - 1) / qt + pb->num_seqs;
+  const int64_t wgs = tiles * pb->num_kv_heads;
+  const int64_t run_keys = 32 * (int64_t)pb->head_dim;
+  int64_t s = ((int64_t)pb->max_context_len + run_keys - 1) / run_keys;
+  const int64_t s_wgs = 2048 / (wgs > 0 ? wgs : 1);
+  if (s > s_wgs) s = s_wgs;
+  if (s > pa::kMaxTileSplits) s = pa::kMaxTileSplits;
+  return s < 1 ? 1 : (int)s;
 }
 
 // pa_prefill for short query runs, and pa_decode at G = 32
@@ -417,16 +448,22 @@ pa_status pa_select_tiles(const pa_problem* problem, pa_tiles* out, size_t* work
     // single-token sequences take the decode table's grid choice
     t.variant = (problem->out_dtype == PA_FP32 ? pa::kVariantPreciseP : 0) |
                 pa::kVariantSeparateMerge | (dc.variant & pa::kVariantEvenWork);
-    // Split query tiles only in batches without single-token sequences:
-    // measured on gfx950, decode workgroups already use the CUs that a few
+    // Query tiles are not split when single-token sequences run as decode
+    // workgroups: measured on gfx950, those already use the CUs that a few
     // long query tiles leave idle, and splitting the tiles then only adds
     // partial traffic (mixed 16 decodes + 2x512-token chunks: 255 us whole,
     // 295 us with two runs per tile; the chunks alone: 197 us -> 134 us).
-    t.tile_splits = may_hold_decode_rows(problem)
-                        ? 1
-                        : pa::table_prefill_splits(problem->total_query_tokens,
-                                                   t.q_tokens_per_tile, problem->num_kv_heads,
-                                                   problem->max_context_len, problem->head_dim);
+    // Where single-token sequences are query tiles themselves, their long
+    // key runs are split (mixed_tile_splits).
+    if (decode_rows_apart(problem)) {
+      t.tile_splits = 1;
+    } else {
+      t.tile_splits = pa::table_prefill_splits(problem->total_query_tokens, t.q_tokens_per_tile,
+                                               problem->num_kv_heads, problem->max_context_len,
+                                               problem->head_dim);
+      if (may_hold_decode_rows(problem))
+        t.tile_splits = std::max(t.tile_splits, mixed_tile_splits(problem));
+    }
   }
   *out = t;
   return pa_workspace_size(problem, &t, workspace_bytes);
@@ -491,8 +528,7 @@ pa_status pa_prefill(const pa_problem* problem, const pa_tiles* tiles, const voi
   // unified launch G = 16 has no decode workgroups: its single-token
   // sequences take the prefill tiles.
   const bool decode_only = problem->max_query_len <= 1;
-  const bool decode_rows =
-      decode_only || (may_hold_decode_rows(problem) && G <= 8 && problem->head_dim == kHeadDim);
+  const bool decode_rows = decode_only || decode_rows_apart(problem);
   const int S = decode_rows ? tiles->num_splits : 1;
   const bool even = decode_rows && even_grid(tiles);
   const int TS = tile_splits_of(problem, tiles);

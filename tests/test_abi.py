@@ -76,6 +76,22 @@ def test_select_tiles_decode_and_prefill(lib):
     st, t, ws = _select(lib, _problem(num_seqs=18, max_query_len=512, total_query_tokens=T + 16,
                                       max_context_len=16384, max_blocks_per_seq=1024))
     assert st == pa.PA_OK and t.tile_splits == 1 and t.num_splits > 1
+    # where single-token sequences are query tiles of their own (head dims 64
+    # and 256, G = 16), their key runs are split: about 32 * head_dim keys a
+    # run, at most eight workgroups per CU in all
+    mixed = dict(num_seqs=18, max_query_len=512, total_query_tokens=T + 16,
+                 max_context_len=16384, max_blocks_per_seq=1024)
+    for kw, want in ((dict(head_dim=64, kv_stride_page=16 * 8 * 64, kv_stride_token=8 * 64,
+                           kv_stride_head=64), 7),
+                     (dict(num_q_heads=64, num_kv_heads=4, kv_stride_page=16 * 4 * 128,
+                           kv_stride_token=4 * 128), 4),
+                     (dict(head_dim=256, kv_stride_page=16 * 8 * 256, kv_stride_token=8 * 256,
+                           kv_stride_head=256), 2)):
+        st, t, ws = _select(lib, _problem(**mixed, **kw))
+        assert st == pa.PA_OK and t.tile_splits == want, (kw, t.tile_splits)
+        D = kw.get("head_dim", 128)
+        Hq = kw.get("num_q_heads", 32)
+        assert ws >= (T + 16) * Hq * t.tile_splits * (D + 1) * 4
 
 
 @pytest.mark.parametrize("field,value,status", [

@@ -3,8 +3,10 @@
 Decode and short query runs at these head dims run on the short-run kernel
 (one Q-block per (sequence, kv head) unit, MFMA for both products); the
 paged append copies rows of any head dim bit for bit.  Longer query runs
-take the query-tile kernel, built for head dims 64 and 128: at 256
-pa_prefill reports them as unsupported.
+take the query-tile kernel (256-row Q-blocks at head dim 64, 128-row
+Q-blocks of four wavefronts at 256).  In a mixed batch at these head dims
+the single-token sequences are query tiles of their own, whose key runs the
+library's launch splits.
 """
 import numpy as np
 import pytest
@@ -198,3 +200,28 @@ def test_prefill_head_dim_256_dominant_logit_bitexact(dev):
             ok = (torch.equal(got.view(torch.int16), want.view(torch.int16))
                   if dt == torch.bfloat16 else torch.equal(got, want))
             assert ok, f"seq {s} t*={t} {dt}"
+
+
+@pytest.mark.parametrize("shape", ["d64", "d256", "g16"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_mixed_batch_split_query_tiles(dev, shape, out_dtype):
+    """A mixed batch whose single-token sequences are query tiles of their own
+    (head dims 64 and 256, and G = 16 at head dim 128): the library's own
+    launch splits the query tiles' key runs, and every row matches the
+    oracle (bf16 output without LSE, the benchmark's launch; fp32 output
+    with LSE)."""
+    log(f"[mixed batch, split query tiles, {shape}, {out_dtype}]")
+    kw = {"d64": dict(head_dim=64), "d256": dict(head_dim=256),
+          "g16": dict(num_q_heads=64, num_kv_heads=4)}[shape]
+    ctx = [9000, 17, 6100, 2500, 1, 8191, 2100, 700]
+    ql = [1, 1, 1, 120, 1, 1, 64, 1]
+    spec = workloads.small_spec(f"mix_{shape}", seed=2100 + 7 * len(kw) + len(shape),
+                                contexts=ctx, queries=ql, decode_layout=False, **kw)
+    b = workloads.generate(spec, dev)
+    pb = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
+                         b.max_context_len, b.max_query_len, causal=True, out_dtype=out_dtype)
+    tiles, _ = pa.select_tiles(pb)
+    assert tiles.tile_splits > 1, tiles.as_dict()
+    with_lse = out_dtype == torch.float32
+    out, lse = run_prefill(b, out_dtype, with_lse=with_lse, stale_workspace=True)
+    compare(b, out, lse, label=f"mixed {shape} ts={tiles.tile_splits} {out_dtype}")
