@@ -56,10 +56,10 @@ TRAFFIC = {
 # The same for one pa_prefill call (unified kernel, + merges when present).
 PREFILL_TRAFFIC = {
     # unified_kernel<4,false,128> (profiles/prefill_chunk2048_hbm_counters.md)
-    "prefill_chunk2048": 184975394,
+    "prefill_chunk2048": 184939303,
     # unified_kernel<4,false,128> + splitkv_reduce_kernel
     # (profiles/mixed_unified_hbm_counters.md)
-    "mixed_unified": 643197832,
+    "mixed_unified": 643197379,
     # verify_kernel<4,1,false,128> + unit_merge_kernel
     # (profiles/spec_verify_b64_hbm_counters.md)
     "spec_verify_b64": 1203498318,
