@@ -140,7 +140,9 @@ typedef struct pa_tiles {
   int32_t tile_splits;       /* pa_prefill: each query tile's keys are cut into     */
                              /* this many runs of whole 32-key tiles (0 or 1: one   */
                              /* run, at most 8), merged by log-sum-exp; it spreads  */
-                             /* a few long-prefix chunks over the whole chip         */
+                             /* a few long-prefix chunks over the whole chip, and    */
+                             /* the long single-token tiles of mixed batches that   */
+                             /* have no decode workgroups                            */
 } pa_tiles;
 
 /* Pick the launch shape for a problem from the built-in table (the offline
@@ -229,7 +231,9 @@ pa_status pa_decode_noalloc(const pa_problem* problem, const pa_tiles* tiles, co
  * split), which return at once for sequences whose query length is not 1.
  * Their partials are merged by a second kernel when tiles->num_splits > 1.
  * Otherwise (G = 16 or 32, head dims 64 and 256) single-token sequences
- * take the tile path.
+ * take the tile path, one tile each; pa_select_tiles then splits the query
+ * tiles' keys (tile_splits, about 32 * head_dim keys a run) so that the
+ * longest such tile does not set the launch time.
  * The host picks the kernels from the problem's bounds alone:
  *   - max_query_len <= 1 (G <= 16): the decode kernels, with query_start_loc
  *     mapping the rows (sequences with no query token are skipped);
