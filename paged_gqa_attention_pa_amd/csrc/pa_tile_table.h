@@ -144,7 +144,9 @@ inline int table_short_splits(int num_seqs, int num_kv_heads, int max_context_le
   return decode_splits;
 }
 
-// Prefill tile_splits for a batch without single-token sequences.
+// Prefill tile_splits from the sweep of batches of query tiles (swept without
+// single-token sequences; pa_select_tiles raises it for mixed batches whose
+// single-token sequences run as query tiles).
 inline int table_prefill_splits(int64_t total_query_tokens, int q_tile, int num_kv_heads,
                                  int max_context_len, int head_dim) {
   const int64_t wgs = (total_query_tokens + q_tile - 1) / q_tile * num_kv_heads;
