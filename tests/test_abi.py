@@ -92,6 +92,13 @@ def test_select_tiles_decode_and_prefill(lib):
         D = kw.get("head_dim", 128)
         Hq = kw.get("num_q_heads", 32)
         assert ws >= (T + 16) * Hq * t.tile_splits * (D + 1) * 4
+    # a mixed batch that already fills the chip (far more than eight query
+    # tiles per CU) keeps its tiles whole
+    st, t, ws = _select(lib, _problem(num_seqs=200, max_query_len=2048, total_query_tokens=200000,
+                                      max_context_len=16384, max_blocks_per_seq=1024,
+                                      head_dim=64, kv_stride_page=16 * 8 * 64,
+                                      kv_stride_token=8 * 64, kv_stride_head=64))
+    assert st == pa.PA_OK and t.tile_splits == 1
 
 
 @pytest.mark.parametrize("field,value,status", [
