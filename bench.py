@@ -22,6 +22,7 @@ Then the paged append, and the fp64 oracle timed on the host cores.
     python bench.py [--gpus 1] [--steps 60] [--warmup 10]
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -96,6 +97,11 @@ def parse():
                     help="time only pa_cache_append on --prefill-workload (for profiling)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill workload (profiling runs)")
+    ap.add_argument("--prefill-shape", default="", choices=("",) + tuple(PREFILL_SHAPES),
+                    help="--prefill-only at another shape: head dim 64 or 256, or G = 16 "
+                         "(64 q / 4 KV heads), same lengths")
+    ap.add_argument("--prefill-tile-splits", type=int, default=-1,
+                    help="--prefill-only with pa_tiles.tile_splits forced (-1 = table)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 4 plain device copies of MIB MiB (a known-size "
                          "kernel for scaling HBM byte counters)")
@@ -256,8 +262,25 @@ def roofline(nbytes, flops, ms, traffic):
             "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic}
 
 
+# Other shapes of a prefill workload (profiling runs): same lengths and seed.
+PREFILL_SHAPES = {"d64": dict(head_dim=64), "d256": dict(head_dim=256),
+                  "g16": dict(num_q_heads=64, num_kv_heads=4)}
+
+
+def shaped_workload(workloads, name, shape):
+    """Name of workload `name` at `shape` (a PREFILL_SHAPES key; "" = as
+    defined), registered in workloads.WORKLOADS on first use."""
+    if not shape:
+        return name
+    shaped = f"{name}_{shape}"
+    if shaped not in workloads.WORKLOADS:
+        workloads.WORKLOADS[shaped] = dataclasses.replace(
+            workloads.WORKLOADS[name], name=shaped, **PREFILL_SHAPES[shape])
+    return shaped
+
+
 def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2048",
-                  copies=3, layout="head_major"):
+                  copies=3, layout="head_major", tile_splits=-1):
     """One pa_prefill call per step, four steps per graph replay.  Each step
     reads a different copy of Q and of the pools and writes a different
     output (`copies` of them, together larger than the 256 MiB Infinity
@@ -268,6 +291,9 @@ def bench_prefill(torch, pa, workloads, dev, steps, warmup, name="prefill_chunk2
     problem = pa.make_problem(b.q, b.k_pool, b.block_tables, b.num_seqs, spec.scale,
                               max_ctx, max_q, causal=spec.causal)
     tiles, ws = pa.select_tiles(problem)
+    if tile_splits >= 0:
+        tiles.tile_splits = tile_splits
+        ws = pa.workspace_size(problem, tiles)
     workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
     sets = [(b.q, b.k_pool, b.v_pool, torch.empty(b.q.shape, dtype=torch.bfloat16, device=dev))]
     for _ in range(max(1, copies) - 1):
@@ -509,7 +535,9 @@ def main():
         return
     if args.prefill_only:
         pre = bench_prefill(torch, pa, workloads, dev, args.steps, args.warmup,
-                            name=args.prefill_workload, layout=args.layout)
+                            name=shaped_workload(workloads, args.prefill_workload,
+                                                 args.prefill_shape),
+                            layout=args.layout, tile_splits=args.prefill_tile_splits)
         note(f"prefill: {pre['value']} TFLOP/s")
         calibrate_copy(torch, dev, args.calibrate_copy)
         print(json.dumps(pre), flush=True)

@@ -122,3 +122,26 @@ def test_bench_layout_default_and_choices(monkeypatch):
     monkeypatch.setattr(sys, "argv", ["bench.py", "--layout", "token_major"])
     assert bench.parse().layout == "token_major"
     assert set(workloads.KV_LAYOUTS) == {"head_major", "token_major"}
+
+
+def test_prefill_shape_options(monkeypatch):
+    """--prefill-shape re-shapes the prefill workload for profiling runs (same
+    lengths and seed, another head dim or grouping); --prefill-tile-splits
+    forces the query-tile split count."""
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert a.prefill_shape == "" and a.prefill_tile_splits == -1
+    assert bench.shaped_workload(workloads, "mixed_unified", "") == "mixed_unified"
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--prefill-only", "--prefill-workload",
+                                      "mixed_unified", "--prefill-shape", "g16",
+                                      "--prefill-tile-splits", "1"])
+    a = bench.parse()
+    assert a.prefill_shape == "g16" and a.prefill_tile_splits == 1
+    base = workloads.WORKLOADS["mixed_unified"]
+    for shape, want in (("d64", (32, 8, 64)), ("d256", (32, 8, 256)), ("g16", (64, 4, 128))):
+        name = bench.shaped_workload(workloads, "mixed_unified", shape)
+        spec = workloads.WORKLOADS[name]
+        assert (spec.num_q_heads, spec.num_kv_heads, spec.head_dim) == want
+        assert (spec.seed, spec.fixed, spec.ctx_range, spec.num_draw) == \
+            (base.seed, base.fixed, base.ctx_range, base.num_draw)
+    assert workloads.WORKLOADS["mixed_unified"] is base
