@@ -192,7 +192,8 @@ bool decode_rows_apart(const pa_problem* pb) {
 // runs hold about 32 * head_dim keys (D = 64: 8 splits, 370 -> 245 us;
 // G = 16 at D = 128: 4 splits, 536 -> 336 us; D = 256: 2 splits,
 // 802 -> 560 us), and splitting further than about eight workgroups per CU
-// (2048 in all) only adds partial traffic.
+// (2048 in all) only adds partial traffic; that cap gives the D = 64 batch
+// 7 splits (249 us).
 int mixed_tile_splits(const pa_problem* pb) {
   const int qt = query_tile_tokens(pb);
   const int64_t tiles = ((int64_t)pb->total_query_tokens + qt - 1) / qt + pb->num_seqs;
